@@ -1,0 +1,166 @@
+/*
+ * think.h - C ABI of the MI355X (gfx950) hot path for query-driven key-cache
+ * channel pruning.
+ *
+ * The four compute calls follow the order in which "ThinK: Thinner Key Cache
+ * by Query-Driven Pruning" (Method details -> Technical framework) states the
+ * method: measure each key channel's relevance to the queries, order the
+ * channels and drop the least relevant, then run inference on the thinner key
+ * cache.  The pages give no API, layout or formula; the readings taken here
+ * are stated at each call.
+ *
+ * Conventions shared by every call
+ *  - Tensor pointers are DEVICE pointers owned by the caller.  Tensors are
+ *    dense, row-major, batch-major, with 16-byte aligned base pointers.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *    Calls enqueue work and return; they never synchronise the stream.
+ *  - The library allocates no device memory and keeps no global state apart
+ *    from a thread-local copy of the last HIP error.
+ *  - Arguments are validated on the host before anything is enqueued.  On an
+ *    error nothing is enqueued and a negative think_status is returned.
+ *  - Outputs must not alias inputs.  Calls on different streams are
+ *    independent and may run concurrently; calls that share a workspace must
+ *    be ordered by the caller.
+ *  - `seq_lens` is device memory: int32 [B], each 1 <= len_b <= S_cap (the
+ *    host cannot check device values; kernels clamp them to [0, S_cap], and a
+ *    length of 0 yields zero scores / zero attention output for that batch).
+ *  - All inputs must be finite.  Padding rows t >= len_b are never read.
+ *  - No float atomics: every result is bitwise reproducible run to run.
+ */
+#ifndef THINK_H
+#define THINK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define THINK_ABI_VERSION 1
+
+#ifndef THINK_API
+#define THINK_API __attribute__((visibility("default")))
+#endif
+
+typedef enum {
+    THINK_OK = 0,
+    THINK_ERR_NULL = -1,        /* a required pointer is NULL */
+    THINK_ERR_SHAPE = -2,       /* inconsistent or out-of-range dimensions */
+    THINK_ERR_KEEP = -3,        /* keep outside [1, head_dim] */
+    THINK_ERR_DTYPE = -4,       /* unknown dtype code */
+    THINK_ERR_UNSUPPORTED = -5, /* valid, but outside what the kernels handle */
+    THINK_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than required */
+    THINK_ERR_HIP = -7          /* a HIP launch failed; see think_last_hip_error */
+} think_status;
+
+typedef enum { THINK_F32 = 0, THINK_BF16 = 1 } think_dtype;
+
+/* Shape of one layer's cache.  Layouts:
+ *   K, V        [B, S_cap, Hkv, D]      (key and value cache)
+ *   Q_w         [B, W, Hq, D]           (observation-window queries)
+ *   K_thin      [B, S_cap, Hkv, keep]   (compacted keys, dense, no padding)
+ *   q, out      [B, Hq, D]              (decode query and attention output)
+ * Query head h reads kv head h / G with G = Hq / Hkv (contiguous groups). */
+typedef struct {
+    int32_t batch;        /* B >= 1 */
+    int32_t n_q_heads;    /* Hq, a multiple of n_kv_heads */
+    int32_t n_kv_heads;   /* Hkv >= 1 */
+    int32_t head_dim;     /* D: a multiple of 8 in [8, 256] */
+    int32_t seq_capacity; /* S_cap >= 1: token stride per sequence of K, V, K_thin */
+    int32_t dtype;        /* think_dtype of K, V, Q_w, q, K_thin and out */
+} think_dims;
+/* Further limits (THINK_ERR_UNSUPPORTED): B <= 65535, Hq/Hkv <= 16,
+ * Hkv*D*element_size <= 32 KiB, S_cap <= 2^28. */
+
+/* Version of this ABI (THINK_ABI_VERSION of the built library). */
+THINK_API int think_abi_version(void);
+
+/* Channels kept at a pruning ratio r in [0, 1): round-half-up of D*(1-r),
+ * clamped to [1, D].  (The pages prune a fixed fraction of channels; this
+ * rounding gives 77 of 128 at 40 %, 51 at 60 %, 64 at 50 %.)  Returns -1 for
+ * D < 1 or r outside [0, 1]. */
+THINK_API int32_t think_keep_from_ratio(int32_t head_dim, double prune_ratio);
+
+/* Bytes of device workspace think_score needs for these dims; 0 if invalid. */
+THINK_API size_t think_score_workspace_bytes(const think_dims *d);
+/* Bytes of device workspace think_decode_attn needs; 0 if invalid. */
+THINK_API size_t think_decode_workspace_bytes(const think_dims *d, int32_t keep);
+
+/*
+ * Stage (a) - per-channel relevance of the key cache to the queries
+ * ("ThinK", Method details -> Technical framework, first step; Key design (1):
+ * relevance is read off the attention logits).  Reading: channel c of kv head
+ * kv contributes the rank-1 term Q_w[:,c] K[:,c]^T to the logits; its score is
+ * that term's Frobenius norm, summed over the G query heads of the group:
+ *   scores[b,kv,c] = sqrt(sum_{t<len_b} K[b,t,kv,c]^2)
+ *                    * sum_{g<G} sqrt(sum_{i<W} Q_w[b,i,kv*G+g,c]^2)
+ * No causal mask; every token t < len_b counts.
+ *   k_cache   [B,S_cap,Hkv,D] dtype    q_obs [B,W,Hq,D] dtype, W = obs_window >= 1
+ *   scores    out, fp32 [B,Hkv,D]
+ *   workspace >= think_score_workspace_bytes(d), 16-byte aligned, caller-owned.
+ * Precision: fp32 squares summed in runs of at most 16 tokens, runs combined
+ * in fp64 in a fixed order; relative error of each score below 1e-6.
+ */
+THINK_API int think_score(const think_dims *d, const void *k_cache, const int32_t *seq_lens,
+                const void *q_obs, int32_t obs_window, float *scores, void *workspace,
+                size_t workspace_bytes, void *stream);
+
+/*
+ * Stage (b) - keep the `keep` most relevant channels of every (b, kv) and
+ * drop the rest ("ThinK", Technical framework, second step; original
+ * abstract: prune the least significant channels).  Order: score descending,
+ * ties to the lower channel index.  Output in ascending channel order.
+ * Reads only batch, n_kv_heads and head_dim of d.
+ *   scores    fp32 [B,Hkv,D] (non-negative, finite)
+ *   kept_idx  out, int32 [B,Hkv,keep], strictly ascending
+ *   near_tie  out, int32 [B,Hkv] or NULL: 1 when keep < D and the keep-th and
+ *             (keep+1)-th scores s_a >= s_b satisfy s_a - s_b <= 1e-5 * s_a
+ *             (evaluated in fp64), so a cutoff decision that rounding could
+ *             flip is reported, not hidden.
+ */
+THINK_API int think_select(const think_dims *d, const float *scores, int32_t keep, int32_t *kept_idx,
+                           int32_t *near_tie, void *stream);
+
+/*
+ * Stage (c) - the thinner key cache ("ThinK", title and Technical framework:
+ * inference proceeds on the pruned key cache).  A byte copy:
+ *   k_thin[b,t,kv,j] = k_cache[b,t,kv,kept_idx[b,kv,j]]   for t < len_b
+ * Rows t >= len_b of k_thin are not written.  kept_idx entries must lie in
+ * [0, D) (values outside are clamped into range, never read out of bounds).
+ *   k_thin    out, [B,S_cap,Hkv,keep] dtype
+ */
+THINK_API int think_compact_k(const think_dims *d, const void *k_cache, const int32_t *seq_lens,
+                    const int32_t *kept_idx, int32_t keep, void *k_thin, void *stream);
+
+/*
+ * Stage (d) - one decode step of attention on the pruned keys ("ThinK",
+ * Technical framework, last step; token generation is bound by memory
+ * bandwidth: "Keyformer: KV Cache Reduction through Key Tokens Selection for
+ * Efficient Generative Inference", original abstract).  Per (b, q head h),
+ * kv = h / G:
+ *   qS[j] = q[b,h,kept_idx[b,kv,j]]
+ *   l_t   = softmax_scale * sum_j qS[j] * k_thin[b,t,kv,j]      (t < len_b)
+ *   out[b,h,:] = sum_t softmax(l)_t * v_cache[b,t,kv,:]
+ * Values are not pruned.  The caller passes softmax_scale (1/sqrt(D) with the
+ * unpruned D reproduces unpruned attention at keep == D).
+ *   q         [B,Hq,D] dtype           out  [B,Hq,D] dtype (written)
+ *   workspace >= think_decode_workspace_bytes(d, keep), 16-byte aligned.
+ * Precision: fp32 accumulation (bf16 matrix-core products for bf16 inputs);
+ * per row ||out - exact||_inf / ||exact||_inf <= 1e-5 (fp32), 2e-2 (bf16).
+ */
+THINK_API int think_decode_attn(const think_dims *d, const void *q, const void *k_thin,
+                      const void *v_cache, const int32_t *seq_lens, const int32_t *kept_idx,
+                      int32_t keep, float softmax_scale, void *out, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/* Static description of a status code. */
+THINK_API const char *think_status_string(int status);
+/* The hipError_t of the last THINK_ERR_HIP on this thread (0 if none). */
+THINK_API int think_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* THINK_H */

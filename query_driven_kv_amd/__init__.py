@@ -1,0 +1,161 @@
+"""MI355X (gfx950) hot path of query-driven key-cache channel pruning (ThinK).
+
+Thin Python layer over the C ABI of include/think.h.  Tensors are torch
+device tensors (torch is used for device memory and streams only); each
+function checks shapes, dtypes, devices and contiguity, builds the
+think_dims descriptor, allocates the workspace when none is passed, and
+calls the HIP library on the current torch stream.
+
+Stages ("ThinK: Thinner Key Cache by Query-Driven Pruning", Method details ->
+Technical framework): think_score -> think_select -> think_compact_k ->
+think_decode_attn.
+"""
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import THINK_BF16, THINK_F32, ThinkError, think_dims
+
+__all__ = ["think_score", "think_select", "think_compact_k", "think_decode_attn",
+           "think_keep_from_ratio", "think_score_workspace_bytes", "think_decode_workspace_bytes",
+           "think_abi_version", "make_dims", "ThinkError", "think_dims", "LIB_PATH"]
+
+LIB_PATH = _lib.LIB_PATH
+_DT = {torch.float32: THINK_F32, torch.bfloat16: THINK_BF16}
+
+
+def _dtype_code(t):
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}; expected float32 or bfloat16") from None
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("tensors must live on the GPU")
+            if not t.is_contiguous():
+                raise ValueError("tensors must be contiguous")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def make_dims(batch, n_q_heads, n_kv_heads, head_dim, seq_capacity, dtype):
+    code = dtype if isinstance(dtype, int) else _DT[dtype]
+    return think_dims(batch, n_q_heads, n_kv_heads, head_dim, seq_capacity, code)
+
+
+def think_abi_version():
+    return _lib.lib.think_abi_version()
+
+
+def think_keep_from_ratio(head_dim, prune_ratio):
+    return _lib.lib.think_keep_from_ratio(int(head_dim), float(prune_ratio))
+
+
+def think_score_workspace_bytes(dims):
+    return _lib.lib.think_score_workspace_bytes(ctypes.byref(dims))
+
+
+def think_decode_workspace_bytes(dims, keep):
+    return _lib.lib.think_decode_workspace_bytes(ctypes.byref(dims), int(keep))
+
+
+def _i32(t, name):
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32")
+
+
+def think_score(k_cache, seq_lens, q_obs, *, scores=None, workspace=None, stream=None):
+    """Stage (a).  k_cache [B,S_cap,Hkv,D], seq_lens int32 [B] (device),
+    q_obs [B,W,Hq,D] -> scores fp32 [B,Hkv,D]."""
+    _dev(k_cache, seq_lens, q_obs, scores, workspace)
+    _i32(seq_lens, "seq_lens")
+    B, S, Hkv, D = k_cache.shape
+    Bq, W, Hq, Dq = q_obs.shape
+    if (Bq, Dq) != (B, D) or q_obs.dtype != k_cache.dtype or tuple(seq_lens.shape) != (B,):
+        raise ValueError("shape or dtype mismatch between k_cache, q_obs and seq_lens")
+    dims = make_dims(B, Hq, Hkv, D, S, _dtype_code(k_cache))
+    if scores is None:
+        scores = torch.empty(B, Hkv, D, dtype=torch.float32, device=k_cache.device)
+    elif scores.dtype != torch.float32 or tuple(scores.shape) != (B, Hkv, D):
+        raise ValueError("scores must be float32 [B,Hkv,D]")
+    need = think_score_workspace_bytes(dims)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=k_cache.device)
+    _lib.check("think_score", _lib.lib.think_score(
+        ctypes.byref(dims), _p(k_cache), _p(seq_lens), _p(q_obs), W, _p(scores), _p(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return scores
+
+
+def think_select(scores, keep, *, kept_idx=None, near_tie=None, want_near_tie=True, stream=None):
+    """Stage (b).  scores fp32 [B,Hkv,D] -> (kept_idx int32 [B,Hkv,keep], near_tie int32 [B,Hkv])."""
+    _dev(scores, kept_idx, near_tie)
+    if scores.dtype != torch.float32 or scores.dim() != 3:
+        raise ValueError("scores must be float32 [B,Hkv,D]")
+    B, Hkv, D = scores.shape
+    dims = make_dims(B, Hkv, Hkv, D, 1, THINK_F32)
+    if kept_idx is None:
+        kept_idx = torch.empty(B, Hkv, max(int(keep), 0), dtype=torch.int32, device=scores.device)
+    if want_near_tie and near_tie is None:
+        near_tie = torch.empty(B, Hkv, dtype=torch.int32, device=scores.device)
+    _lib.check("think_select", _lib.lib.think_select(
+        ctypes.byref(dims), _p(scores), int(keep), _p(kept_idx), _p(near_tie), _stream(stream)))
+    return kept_idx, near_tie
+
+
+def think_compact_k(k_cache, seq_lens, kept_idx, *, k_thin=None, stream=None):
+    """Stage (c).  k_cache [B,S_cap,Hkv,D], kept_idx int32 [B,Hkv,keep] ->
+    k_thin [B,S_cap,Hkv,keep] (rows t >= len_b untouched)."""
+    _dev(k_cache, seq_lens, kept_idx, k_thin)
+    _i32(seq_lens, "seq_lens")
+    _i32(kept_idx, "kept_idx")
+    B, S, Hkv, D = k_cache.shape
+    keep = kept_idx.shape[-1]
+    if tuple(kept_idx.shape) != (B, Hkv, keep):
+        raise ValueError("kept_idx must be [B,Hkv,keep]")
+    dims = make_dims(B, Hkv, Hkv, D, S, _dtype_code(k_cache))
+    if k_thin is None:
+        k_thin = torch.empty(B, S, Hkv, keep, dtype=k_cache.dtype, device=k_cache.device)
+    elif tuple(k_thin.shape) != (B, S, Hkv, keep) or k_thin.dtype != k_cache.dtype:
+        raise ValueError("k_thin must be [B,S_cap,Hkv,keep] of the cache dtype")
+    _lib.check("think_compact_k", _lib.lib.think_compact_k(
+        ctypes.byref(dims), _p(k_cache), _p(seq_lens), _p(kept_idx), keep, _p(k_thin),
+        _stream(stream)))
+    return k_thin
+
+
+def think_decode_attn(q, k_thin, v_cache, seq_lens, kept_idx, softmax_scale, *, out=None,
+                      workspace=None, stream=None):
+    """Stage (d).  q [B,Hq,D], k_thin [B,S_cap,Hkv,keep], v_cache [B,S_cap,Hkv,D],
+    kept_idx int32 [B,Hkv,keep] -> out [B,Hq,D] (dtype of q)."""
+    _dev(q, k_thin, v_cache, seq_lens, kept_idx, out, workspace)
+    _i32(seq_lens, "seq_lens")
+    _i32(kept_idx, "kept_idx")
+    B, Hq, D = q.shape
+    _, S, Hkv, keep = k_thin.shape
+    if (tuple(v_cache.shape) != (B, S, Hkv, D) or tuple(kept_idx.shape) != (B, Hkv, keep)
+            or k_thin.dtype != q.dtype or v_cache.dtype != q.dtype):
+        raise ValueError("shape or dtype mismatch between q, k_thin, v_cache and kept_idx")
+    dims = make_dims(B, Hq, Hkv, D, S, _dtype_code(q))
+    if out is None:
+        out = torch.empty(B, Hq, D, dtype=q.dtype, device=q.device)
+    need = think_decode_workspace_bytes(dims, keep)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _lib.check("think_decode_attn", _lib.lib.think_decode_attn(
+        ctypes.byref(dims), _p(q), _p(k_thin), _p(v_cache), _p(seq_lens), _p(kept_idx), int(keep),
+        float(softmax_scale), _p(out), _p(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return out

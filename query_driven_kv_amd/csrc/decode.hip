@@ -1,0 +1,193 @@
+// decode.hip - stage (d): one decode step of attention on the pruned keys
+// ("ThinK: Thinner Key Cache by Query-Driven Pruning", Method details ->
+// Technical framework, last step; the step is memory-bandwidth bound per
+// "Keyformer: KV Cache Reduction through Key Tokens Selection for Efficient
+// Generative Inference", original abstract).
+//
+//   qS[j] = q[b,h,kept_idx[b,kv,j]]
+//   l_t   = scale * sum_j qS[j] * k_thin[b,t,kv,j]       t < len_b
+//   out   = softmax(l) . V[b,:,kv,:]                     (values unpruned)
+//
+// Split-K ("flash decoding") over tokens: a workgroup owns one token chunk of
+// one (b, kv head) and all G query heads of that group, so the G heads share
+// every byte of K_thin and V it streams.  It writes per-head partials
+// (running max m, sum l, unnormalised o[D]) to the workspace; a combine
+// kernel merges the chunks of each (b, h) in ascending chunk order.
+//
+// This file holds the general kernel (any dtype, any keep, G <= 16).  The
+// bf16 matrix-core kernel for the bandwidth-critical shapes is in
+// decode_mfma.hip and writes the same partial records.
+#include "think_common.h"
+
+namespace thinkkv {
+
+// defined in decode_mfma.hip
+bool mfma_decode_supported(const think_dims& d, int keep);
+int mfma_decode_chunk(const think_dims& d, int keep);
+hipError_t launch_decode_mfma(const think_dims& d, const DecodeGeom& g, const void* q,
+                              const void* k_thin, const void* v_cache, const int32_t* seq_lens,
+                              const int32_t* kept_idx, int keep, float scale, float* partials,
+                              hipStream_t s);
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kChunk = 256;    // tokens per workgroup (general kernel)
+constexpr int kMaxG = 16;
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_decode_partial(
+        const typename Elem<DT>::T* __restrict__ q, const typename Elem<DT>::T* __restrict__ k_thin,
+        const typename Elem<DT>::T* __restrict__ v_cache, const int32_t* __restrict__ seq_lens,
+        const int32_t* __restrict__ kept_idx, int s_cap, int Hkv, int G, int D, int keep,
+        float scale, int nsplit, int rec, float* __restrict__ partials) {
+    using E = Elem<DT>;
+    const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+    const int len = clamp_len(seq_lens, b, s_cap);
+    const int t0 = split * kChunk;
+    if (t0 >= len) return;                       // the combine stops before this chunk
+    const int nt = min(kChunk, len - t0);
+    const int Hq = Hkv * G;
+    const int tid = threadIdx.x;
+
+    __shared__ float qs[kMaxG * 256];            // gathered query, [g][j]
+    __shared__ float p[kMaxG * kChunk];          // logits, then probabilities, [g][t]
+    __shared__ float mrow[kMaxG], lrow[kMaxG];
+
+    for (int i = tid; i < G * keep; i += kThreads) {
+        const int g = i / keep, j = i - g * keep;
+        int c = kept_idx[((size_t)b * Hkv + kv) * keep + j];
+        c = c < 0 ? 0 : (c >= D ? D - 1 : c);
+        qs[i] = E::load(q, ((size_t)b * Hq + kv * G + g) * D + c);
+    }
+    __syncthreads();
+
+    if (tid < nt) {
+        const size_t kr = (((size_t)b * s_cap + t0 + tid) * Hkv + kv) * keep;
+        float acc[kMaxG];
+#pragma unroll
+        for (int g = 0; g < kMaxG; ++g) acc[g] = 0.0f;
+        for (int j = 0; j < keep; ++j) {
+            const float x = E::load(k_thin, kr + j);
+#pragma unroll
+            for (int g = 0; g < kMaxG; ++g)
+                if (g < G) acc[g] = fmaf(qs[g * keep + j], x, acc[g]);
+        }
+#pragma unroll
+        for (int g = 0; g < kMaxG; ++g)
+            if (g < G) p[g * kChunk + tid] = acc[g] * scale;
+    }
+    __syncthreads();
+
+    if (tid < G) {
+        float* pr = p + tid * kChunk;
+        float m = pr[0];
+        for (int t = 1; t < nt; ++t) m = fmaxf(m, pr[t]);
+        float l = 0.0f;
+        for (int t = 0; t < nt; ++t) {
+            const float e = expf(pr[t] - m);
+            pr[t] = e;
+            l += e;
+        }
+        mrow[tid] = m;
+        lrow[tid] = l;
+    }
+    __syncthreads();
+
+    for (int d = tid; d < D; d += kThreads) {
+        float o[kMaxG];
+#pragma unroll
+        for (int g = 0; g < kMaxG; ++g) o[g] = 0.0f;
+        for (int t = 0; t < nt; ++t) {
+            const float v = E::load(v_cache, (((size_t)b * s_cap + t0 + t) * Hkv + kv) * D + d);
+#pragma unroll
+            for (int g = 0; g < kMaxG; ++g)
+                if (g < G) o[g] = fmaf(p[g * kChunk + t], v, o[g]);
+        }
+#pragma unroll
+        for (int g = 0; g < kMaxG; ++g)
+            if (g < G)
+                partials[(((size_t)b * Hq + kv * G + g) * nsplit + split) * rec + 4 + d] = o[g];
+    }
+    if (tid < G) {
+        float* r = partials + (((size_t)b * Hq + kv * G + tid) * nsplit + split) * rec;
+        r[0] = mrow[tid];
+        r[1] = lrow[tid];
+    }
+}
+
+// Merge the chunks of one (b, h) in ascending chunk order.
+template <int DT>
+__global__ __launch_bounds__(256) void k_decode_combine(
+        const float* __restrict__ partials, const int32_t* __restrict__ seq_lens, int s_cap,
+        int chunk, int nsplit, int rec, int D, typename Elem<DT>::T* __restrict__ out) {
+    using E = Elem<DT>;
+    const int h = blockIdx.x, b = blockIdx.y, Hq = gridDim.x;
+    const int len = clamp_len(seq_lens, b, s_cap);
+    const int ns = (len + chunk - 1) / chunk;
+    const float* base = partials + ((size_t)b * Hq + h) * nsplit * rec;
+    for (int d = threadIdx.x; d < D; d += blockDim.x) {
+        float res = 0.0f;
+        if (ns > 0) {
+            float M = base[0];
+            for (int s = 1; s < ns; ++s) M = fmaxf(M, base[(size_t)s * rec]);
+            float L = 0.0f, O = 0.0f;
+            for (int s = 0; s < ns; ++s) {
+                const float* r = base + (size_t)s * rec;
+                const float w = expf(r[0] - M);
+                L = fmaf(w, r[1], L);
+                O = fmaf(w, r[4 + d], O);
+            }
+            res = O / L;
+        }
+        E::store(out, ((size_t)b * Hq + h) * D + d, res);
+    }
+}
+
+}  // namespace
+
+DecodeGeom decode_geom(const think_dims& d, int keep) {
+    DecodeGeom g{};
+    g.mfma = mfma_decode_supported(d, keep);
+    g.chunk = g.mfma ? mfma_decode_chunk(d, keep) : kChunk;
+    g.nsplit = (d.seq_capacity + g.chunk - 1) / g.chunk;
+    g.rec = d.head_dim + 4;
+    g.ws_bytes = (size_t)d.batch * d.n_q_heads * g.nsplit * g.rec * sizeof(float);
+    return g;
+}
+
+hipError_t launch_decode(const think_dims& d, const DecodeGeom& g, const void* q,
+                         const void* k_thin, const void* v_cache, const int32_t* seq_lens,
+                         const int32_t* kept_idx, int keep, float scale, void* out,
+                         float* partials, hipStream_t s) {
+    const int G = d.n_q_heads / d.n_kv_heads;
+    dim3 grid(g.nsplit, d.n_kv_heads, d.batch);
+    dim3 cgrid(d.n_q_heads, d.batch);
+    const int cthreads = d.head_dim < 256 ? d.head_dim : 256;
+    if (g.mfma) {
+        hipError_t e = launch_decode_mfma(d, g, q, k_thin, v_cache, seq_lens, kept_idx, keep,
+                                          scale, partials, s);
+        if (e != hipSuccess) return e;
+        k_decode_combine<THINK_BF16><<<cgrid, cthreads, 0, s>>>(
+            partials, seq_lens, d.seq_capacity, g.chunk, g.nsplit, g.rec, d.head_dim,
+            (uint16_t*)out);
+    } else if (d.dtype == THINK_BF16) {
+        k_decode_partial<THINK_BF16><<<grid, kThreads, 0, s>>>(
+            (const uint16_t*)q, (const uint16_t*)k_thin, (const uint16_t*)v_cache, seq_lens,
+            kept_idx, d.seq_capacity, d.n_kv_heads, G, d.head_dim, keep, scale, g.nsplit, g.rec,
+            partials);
+        k_decode_combine<THINK_BF16><<<cgrid, cthreads, 0, s>>>(
+            partials, seq_lens, d.seq_capacity, g.chunk, g.nsplit, g.rec, d.head_dim,
+            (uint16_t*)out);
+    } else {
+        k_decode_partial<THINK_F32><<<grid, kThreads, 0, s>>>(
+            (const float*)q, (const float*)k_thin, (const float*)v_cache, seq_lens, kept_idx,
+            d.seq_capacity, d.n_kv_heads, G, d.head_dim, keep, scale, g.nsplit, g.rec, partials);
+        k_decode_combine<THINK_F32><<<cgrid, cthreads, 0, s>>>(
+            partials, seq_lens, d.seq_capacity, g.chunk, g.nsplit, g.rec, d.head_dim,
+            (float*)out);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace thinkkv

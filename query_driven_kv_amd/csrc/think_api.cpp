@@ -1,0 +1,133 @@
+// think_api.cpp - host side of the C ABI declared in include/think.h:
+// argument validation (before anything is enqueued), workspace sizing,
+// dispatch to the gfx950 kernels and HIP-error mapping.
+#include <math.h>
+#include <stdint.h>
+
+#include "think_common.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int check_dims(const think_dims* d) {
+    if (!d) return THINK_ERR_NULL;
+    if (d->dtype != THINK_F32 && d->dtype != THINK_BF16) return THINK_ERR_DTYPE;
+    if (d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->head_dim < 1 ||
+        d->seq_capacity < 1)
+        return THINK_ERR_SHAPE;
+    if (d->n_q_heads % d->n_kv_heads != 0) return THINK_ERR_SHAPE;
+    if (d->head_dim % 8 != 0 || d->head_dim > 256) return THINK_ERR_UNSUPPORTED;
+    if (d->batch > 65535) return THINK_ERR_UNSUPPORTED;
+    if (d->n_q_heads / d->n_kv_heads > 16) return THINK_ERR_UNSUPPORTED;
+    if ((int64_t)d->n_kv_heads * d->head_dim * thinkkv::elem_bytes(d->dtype) > 32768)
+        return THINK_ERR_UNSUPPORTED;
+    if (d->seq_capacity > (1 << 28)) return THINK_ERR_UNSUPPORTED;
+    return THINK_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return THINK_OK;
+    g_last_hip_error = (int)e;
+    return THINK_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int think_abi_version(void) { return THINK_ABI_VERSION; }
+
+int32_t think_keep_from_ratio(int32_t head_dim, double prune_ratio) {
+    if (head_dim < 1 || !(prune_ratio >= 0.0) || !(prune_ratio <= 1.0)) return -1;
+    double k = floor((double)head_dim * (1.0 - prune_ratio) + 0.5);
+    if (k < 1.0) k = 1.0;
+    if (k > head_dim) k = head_dim;
+    return (int32_t)k;
+}
+
+size_t think_score_workspace_bytes(const think_dims* d) {
+    if (check_dims(d) != THINK_OK) return 0;
+    return thinkkv::score_geom(*d).ws_bytes;
+}
+
+size_t think_decode_workspace_bytes(const think_dims* d, int32_t keep) {
+    if (check_dims(d) != THINK_OK || keep < 1 || keep > d->head_dim) return 0;
+    return thinkkv::decode_geom(*d, keep).ws_bytes;
+}
+
+int think_score(const think_dims* d, const void* k_cache, const int32_t* seq_lens,
+                const void* q_obs, int32_t obs_window, float* scores, void* workspace,
+                size_t workspace_bytes, void* stream) {
+    int st = check_dims(d);
+    if (st != THINK_OK) return st;
+    if (!k_cache || !seq_lens || !q_obs || !scores) return THINK_ERR_NULL;
+    if (obs_window < 1) return THINK_ERR_SHAPE;
+    if (!aligned16(k_cache)) return THINK_ERR_UNSUPPORTED;
+    const thinkkv::ScoreGeom g = thinkkv::score_geom(*d);
+    if (!workspace || workspace_bytes < g.ws_bytes || !aligned16(workspace))
+        return THINK_ERR_WORKSPACE;
+    return hip_status(thinkkv::launch_score(*d, g, k_cache, seq_lens, q_obs, obs_window, scores,
+                                            (float*)workspace, (hipStream_t)stream));
+}
+
+int think_select(const think_dims* d, const float* scores, int32_t keep, int32_t* kept_idx,
+                 int32_t* near_tie, void* stream) {
+    if (!d) return THINK_ERR_NULL;
+    if (d->batch < 1 || d->n_kv_heads < 1 || d->head_dim < 1) return THINK_ERR_SHAPE;
+    if (d->head_dim % 8 != 0 || d->head_dim > 256 || d->batch > 65535 || d->n_kv_heads > 65535)
+        return THINK_ERR_UNSUPPORTED;
+    if (!scores || !kept_idx) return THINK_ERR_NULL;
+    if (keep < 1 || keep > d->head_dim) return THINK_ERR_KEEP;
+    return hip_status(
+        thinkkv::launch_select(*d, scores, keep, kept_idx, near_tie, (hipStream_t)stream));
+}
+
+int think_compact_k(const think_dims* d, const void* k_cache, const int32_t* seq_lens,
+                    const int32_t* kept_idx, int32_t keep, void* k_thin, void* stream) {
+    int st = check_dims(d);
+    if (st != THINK_OK) return st;
+    if (!k_cache || !seq_lens || !kept_idx || !k_thin) return THINK_ERR_NULL;
+    if (keep < 1 || keep > d->head_dim) return THINK_ERR_KEEP;
+    if (!aligned16(k_cache) || !aligned16(k_thin)) return THINK_ERR_UNSUPPORTED;
+    const thinkkv::CompactGeom g = thinkkv::compact_geom(*d, keep);
+    return hip_status(thinkkv::launch_compact(*d, g, k_cache, seq_lens, kept_idx, keep, k_thin,
+                                              (hipStream_t)stream));
+}
+
+int think_decode_attn(const think_dims* d, const void* q, const void* k_thin,
+                      const void* v_cache, const int32_t* seq_lens, const int32_t* kept_idx,
+                      int32_t keep, float softmax_scale, void* out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    int st = check_dims(d);
+    if (st != THINK_OK) return st;
+    if (!q || !k_thin || !v_cache || !seq_lens || !kept_idx || !out) return THINK_ERR_NULL;
+    if (keep < 1 || keep > d->head_dim) return THINK_ERR_KEEP;
+    if (!aligned16(k_thin) || !aligned16(v_cache) || !aligned16(q)) return THINK_ERR_UNSUPPORTED;
+    const thinkkv::DecodeGeom g = thinkkv::decode_geom(*d, keep);
+    if (!workspace || workspace_bytes < g.ws_bytes || !aligned16(workspace))
+        return THINK_ERR_WORKSPACE;
+    return hip_status(thinkkv::launch_decode(*d, g, q, k_thin, v_cache, seq_lens, kept_idx, keep,
+                                             softmax_scale, out, (float*)workspace,
+                                             (hipStream_t)stream));
+}
+
+const char* think_status_string(int status) {
+    switch (status) {
+        case THINK_OK: return "ok";
+        case THINK_ERR_NULL: return "a required pointer is NULL";
+        case THINK_ERR_SHAPE: return "inconsistent or out-of-range dimensions";
+        case THINK_ERR_KEEP: return "keep outside [1, head_dim]";
+        case THINK_ERR_DTYPE: return "unknown dtype";
+        case THINK_ERR_UNSUPPORTED: return "shape, alignment or size outside what the kernels handle";
+        case THINK_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case THINK_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+int think_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,105 @@
+// think_common.h - internal helpers shared by the gfx950 kernels and the
+// host-side ABI layer.  Not part of the public interface (see include/think.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "think.h"
+
+namespace thinkkv {
+
+// ---------------------------------------------------------------------------
+// Element access.  bf16 is carried as its 16-bit pattern; widening to fp32 is
+// exact, narrowing rounds to nearest even (inputs are finite).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+template <int DT> struct Elem;
+template <> struct Elem<THINK_F32> {
+    using T = float;
+    static constexpr int kBytes = 4;
+    static constexpr int kPerVec = 4;   // elements per 16-byte vector
+    __device__ static float load(const T* p, size_t i) { return p[i]; }
+    __device__ static void store(T* p, size_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<THINK_BF16> {
+    using T = uint16_t;
+    static constexpr int kBytes = 2;
+    static constexpr int kPerVec = 8;
+    __device__ static float load(const T* p, size_t i) { return bf16_to_f32(p[i]); }
+    __device__ static void store(T* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+
+// Unpack one 16-byte vector into fp32 values.
+__device__ __forceinline__ void unpack(const uint4& v, float (&x)[4], Elem<THINK_F32>) {
+    x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
+    x[2] = __uint_as_float(v.z); x[3] = __uint_as_float(v.w);
+}
+__device__ __forceinline__ void unpack(const uint4& v, float (&x)[8], Elem<THINK_BF16>) {
+    x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+    x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+}
+
+__device__ __forceinline__ int clamp_len(const int32_t* seq_lens, int b, int s_cap) {
+    int n = seq_lens[b];
+    return n < 0 ? 0 : (n > s_cap ? s_cap : n);
+}
+
+inline int elem_bytes(int dtype) { return dtype == THINK_F32 ? 4 : 2; }
+
+// ---------------------------------------------------------------------------
+// Launch geometry, shared by the workspace-size queries and the launchers so
+// that both always agree.
+// ---------------------------------------------------------------------------
+struct ScoreGeom {
+    int nvec;        // 16-byte vectors per token row (Hkv*D*e/16)
+    int ncg;         // column groups of <= 256 vectors
+    int tpw;         // tokens per workgroup
+    int nsplit;      // token splits per sequence
+    size_t ws_bytes; // fp32 partials [B][nsplit][Hkv*D]
+};
+ScoreGeom score_geom(const think_dims& d);
+
+struct DecodeGeom {
+    int chunk;       // tokens per workgroup
+    int nsplit;      // splits per sequence
+    int rec;         // floats per partial record: m, l, 2 pad, o[D]
+    bool mfma;       // bf16 matrix-core kernel
+    size_t ws_bytes; // [B][Hq][nsplit][rec] fp32
+};
+DecodeGeom decode_geom(const think_dims& d, int keep);
+
+struct CompactGeom {
+    int tile;        // tokens per workgroup
+    size_t lds;      // dynamic LDS bytes
+};
+CompactGeom compact_geom(const think_dims& d, int keep);
+
+// ---------------------------------------------------------------------------
+// Launchers (return hipGetLastError() after enqueueing).
+// ---------------------------------------------------------------------------
+hipError_t launch_score(const think_dims& d, const ScoreGeom& g, const void* k_cache,
+                        const int32_t* seq_lens, const void* q_obs, int W, float* scores,
+                        float* partials, hipStream_t s);
+hipError_t launch_select(const think_dims& d, const float* scores, int keep, int32_t* kept_idx,
+                         int32_t* near_tie, hipStream_t s);
+hipError_t launch_compact(const think_dims& d, const CompactGeom& g, const void* k_cache,
+                          const int32_t* seq_lens, const int32_t* kept_idx, int keep,
+                          void* k_thin, hipStream_t s);
+hipError_t launch_decode(const think_dims& d, const DecodeGeom& g, const void* q,
+                         const void* k_thin, const void* v_cache, const int32_t* seq_lens,
+                         const int32_t* kept_idx, int keep, float scale, void* out,
+                         float* partials, hipStream_t s);
+
+}  // namespace thinkkv

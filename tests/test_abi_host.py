@@ -1,0 +1,135 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol that
+include/think.h declares, and its host-side validation returns the documented
+status codes before anything is enqueued (every call below fails validation,
+so no kernel is ever launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "think.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from query_driven_kv_amd import _lib
+    return _lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"THINK_API\s+[\w\s\*]+?\b(think_\w+)\s*\(", text)))
+
+
+def test_header_declarations_are_all_exported(L):
+    names = declared_functions()
+    assert len(names) == 10
+    assert sorted(L.EXPORTS) == names
+    so = ctypes.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(so, n), n
+
+
+def test_only_the_abi_is_exported(L):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    ours = {ln.split()[-1] for ln in out.splitlines() if "think" in ln}
+    assert ours == set(declared_functions())
+
+
+def test_version_and_keep_rounding(L):
+    lib = L.lib
+    assert lib.think_abi_version() == 1
+    assert [lib.think_keep_from_ratio(128, r) for r in (0.4, 0.6, 0.5)] == [77, 51, 64]
+    assert lib.think_keep_from_ratio(16, 0.5) == 8
+    assert lib.think_keep_from_ratio(128, 0.0) == 128
+    assert lib.think_keep_from_ratio(128, 1.0) == 1          # clamped to one channel
+    assert lib.think_keep_from_ratio(5, 0.5) == 3            # half rounds up
+    assert lib.think_keep_from_ratio(0, 0.5) == -1
+    assert lib.think_keep_from_ratio(128, -0.1) == -1
+    assert lib.think_keep_from_ratio(128, float("nan")) == -1
+
+
+def dims(L, B=1, Hq=32, Hkv=8, D=128, S=32768, dt=1):
+    return L.think_dims(B, Hq, Hkv, D, S, dt)
+
+
+def test_workspace_sizes(L):
+    lib = L.lib
+    d = dims(L)
+    ws = lib.think_score_workspace_bytes(ctypes.byref(d))
+    assert ws > 0 and ws % 16 == 0
+    assert ws < 32768 * 8 * 128 * 2 // 10        # partials stay a small fraction of |K|
+    wd = lib.think_decode_workspace_bytes(ctypes.byref(d), 64)
+    assert wd > 0 and wd % 16 == 0
+    assert lib.think_decode_workspace_bytes(ctypes.byref(d), 0) == 0
+    assert lib.think_decode_workspace_bytes(ctypes.byref(d), 129) == 0
+    assert lib.think_score_workspace_bytes(ctypes.byref(dims(L, Hq=30))) == 0
+    assert lib.think_score_workspace_bytes(None) == 0
+
+
+FAKE = ctypes.c_void_p(0x100000)      # never dereferenced: every call fails validation first
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hq=30), -2),                  # Hq not a multiple of Hkv
+    (dict(B=0), -2),
+    (dict(S=0), -2),
+    (dict(dt=7), -4),
+    (dict(D=12), -5),                   # head_dim not a multiple of 8
+    (dict(D=264), -5),
+    (dict(Hq=136, Hkv=8), -5),          # group of 17 query heads
+    (dict(Hkv=65, Hq=65, D=256), -5),   # token row above 32 KiB
+])
+def test_score_rejects_bad_dims(L, kw, status):
+    d = dims(L, **kw)
+    rc = L.lib.think_score(ctypes.byref(d), FAKE, FAKE, FAKE, 32, FAKE, FAKE, 1 << 30, None)
+    assert rc == status
+    assert L.lib.think_compact_k(ctypes.byref(d), FAKE, FAKE, FAKE, 8, FAKE, None) == status
+    assert L.lib.think_decode_attn(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 8, 0.1, FAKE,
+                                   FAKE, 1 << 30, None) == status
+
+
+def test_null_keep_window_workspace_and_alignment(L):
+    lib = L.lib
+    d = dims(L)
+    big = 1 << 30
+    assert lib.think_score(None, FAKE, FAKE, FAKE, 32, FAKE, FAKE, big, None) == -1
+    assert lib.think_score(ctypes.byref(d), None, FAKE, FAKE, 32, FAKE, FAKE, big, None) == -1
+    assert lib.think_score(ctypes.byref(d), FAKE, FAKE, FAKE, 0, FAKE, FAKE, big, None) == -2
+    assert lib.think_score(ctypes.byref(d), FAKE, FAKE, FAKE, 32, FAKE, FAKE, 16, None) == -6
+    assert lib.think_score(ctypes.byref(d), FAKE, FAKE, FAKE, 32, FAKE, None, big, None) == -6
+    assert lib.think_score(ctypes.byref(d), ctypes.c_void_p(0x100002), FAKE, FAKE, 32, FAKE, FAKE,
+                           big, None) == -5
+    for keep in (0, 129):
+        assert lib.think_select(ctypes.byref(d), FAKE, keep, FAKE, None, None) == -3
+        assert lib.think_compact_k(ctypes.byref(d), FAKE, FAKE, FAKE, keep, FAKE, None) == -3
+        assert lib.think_decode_attn(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, keep, 0.1, FAKE,
+                                     FAKE, big, None) == -3
+    assert lib.think_select(ctypes.byref(d), None, 8, FAKE, None, None) == -1
+    assert lib.think_select(ctypes.byref(dims(L, D=12)), FAKE, 8, FAKE, None, None) == -5
+    assert lib.think_compact_k(ctypes.byref(d), FAKE, FAKE, FAKE, 8, None, None) == -1
+    assert lib.think_compact_k(ctypes.byref(d), FAKE, FAKE, FAKE, 8, ctypes.c_void_p(0x100008),
+                               None) == -5
+    assert lib.think_decode_attn(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 8, 0.1, FAKE,
+                                 FAKE, 64, None) == -6
+    assert lib.think_decode_attn(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, 8, 0.1, FAKE,
+                                 FAKE, big, None) == -1
+
+
+def test_status_strings(L):
+    for code in range(-7, 1):
+        assert L.lib.think_status_string(code)
+    assert L.lib.think_status_string(-99) == b"unknown status"
+    assert L.lib.think_last_hip_error() == 0
+
+
+def test_python_layer_checks_before_calling(L):
+    import torch
+    import query_driven_kv_amd as qdk
+    with pytest.raises(ValueError):
+        qdk.think_score(torch.zeros(1, 4, 2, 8), torch.zeros(1, dtype=torch.int32),
+                        torch.zeros(1, 2, 2, 8))          # CPU tensors are refused

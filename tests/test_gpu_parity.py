@@ -1,0 +1,191 @@
+"""GPU parity: every stage of the HIP path against the fp64 oracle on the same
+seeded inputs, stage by stage so a failure points at one kernel.
+
+ (i)   scores within 5e-6 relative of the oracle's fp64 scores
+ (ii)  think_select(GPU scores) == oracle select on the same fp32 scores, bit-exact
+       (indices and near-tie flags)
+ (iii) GPU indices == oracle select on the oracle's scores, except (b, kv)
+       pairs the oracle flags as near ties (listed, never hidden)
+ (iv)  think_compact_k == oracle compaction with the GPU indices, bytewise;
+       padding rows of K_thin untouched
+ (v)   think_decode_attn vs oracle decode (GPU indices, compacted keys):
+       per-row max-abs relative error <= 1e-5 (fp32) / 2e-2 (bf16)
+ (vi)  two runs bit-identical
+Padding rows of every cache hold a NaN sentinel, so a read past len_b shows up.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kvsynth
+import oracle
+from gpu_util import row_rel_err, to_dev, to_host, tol_for
+
+pytestmark = pytest.mark.gpu
+
+SCORE_RTOL = 5e-6
+
+
+def _qdk():
+    import query_driven_kv_amd as qdk
+    return qdk
+
+
+def run_path(L, keep, q, scale):
+    qdk = _qdk()
+    k = to_dev(L["k_cache"])
+    v = to_dev(L["v_cache"])
+    lens = to_dev(L["seq_lens"])
+    qo = to_dev(L["q_obs"])
+    qd = to_dev(q)
+    scores = qdk.think_score(k, lens, qo)
+    idx, tie = qdk.think_select(scores, keep)
+    B, S, Hkv, D = k.shape
+    thin = torch.full((B, S, Hkv, keep), float("nan"), dtype=k.dtype, device=k.device)
+    qdk.think_compact_k(k, lens, idx, k_thin=thin)
+    out = qdk.think_decode_attn(qd, thin, v, lens, idx, scale)
+    torch.cuda.synchronize()
+    return dict(scores=to_host(scores), idx=to_host(idx), tie=to_host(tie), thin=to_host(thin),
+                out=to_host(out))
+
+
+def check_all(cfg, L, keep, q, scale, label):
+    print(f"[parity] {label}: B={cfg.batch} S={cfg.seq_capacity} Hq={cfg.n_q_heads} "
+          f"Hkv={cfg.n_kv_heads} D={cfg.head_dim} keep={keep} {cfg.dtype}", flush=True)
+    g = run_path(L, keep, q, scale)
+    lens = L["seq_lens"]
+    # (i)
+    ref_s = oracle.score(L["k_cache"], lens, L["q_obs"])
+    rel = np.abs(g["scores"].astype(np.float64) - ref_s) / np.maximum(ref_s, 1e-30)
+    assert rel.max() <= SCORE_RTOL, f"score rel err {rel.max():.3e}"
+    # (ii)
+    o_idx, o_tie = oracle.select(g["scores"].astype(np.float64), keep)
+    np.testing.assert_array_equal(g["idx"], o_idx)
+    np.testing.assert_array_equal(g["tie"], o_tie)
+    # (iii)
+    r_idx, r_tie = oracle.select(ref_s, keep)
+    diff = (g["idx"] != r_idx).any(axis=-1)
+    assert not (diff & (r_tie == 0)).any(), "kept set differs outside a reported near tie"
+    near = list(zip(*np.nonzero(r_tie)))
+    if near:
+        print(f"[parity] {label}: near ties at (b, kv) {near}", flush=True)
+    # (iv)
+    sentinel = kvsynth.nan_value(cfg.dtype)
+    ref_thin = oracle.compact(L["k_cache"], lens, g["idx"], fill=sentinel)
+    for b, n in enumerate(lens):
+        np.testing.assert_array_equal(g["thin"][b, :n].view(np.uint8), ref_thin[b, :n].view(np.uint8))
+        assert np.isnan(kvsynth.as_float(g["thin"][b, n:])).all(), "padding rows of K_thin were written"
+    # (v)
+    ref_o = oracle.decode(q, ref_thin, L["v_cache"], lens, g["idx"], scale)
+    err = row_rel_err(g["out"], ref_o)
+    assert err.max() <= tol_for(cfg.dtype), f"decode row error {err.max():.3e}"
+    print(f"[parity] {label}: score rel {rel.max():.2e}, decode row err {err.max():.2e}", flush=True)
+    return g
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama2-7b-layer-4k", "mistral-7b-gqa-32k",
+                                  "batched-ragged-16k"])
+def test_full_config_parity(name):
+    cfg = kvsynth.CONFIGS[name]
+    L = kvsynth.make_layer(cfg, 0)
+    q = kvsynth.decode_q(cfg, 0, 0, L["channel_scale"])
+    scale = np.float32(1.0 / np.sqrt(cfg.head_dim))
+    g1 = check_all(cfg, L, cfg.keep, q, scale, name)
+    # (vi) determinism
+    g2 = run_path(L, cfg.keep, q, scale)
+    for key in g1:
+        np.testing.assert_array_equal(g1[key].view(np.uint8), g2[key].view(np.uint8))
+
+
+def test_llama3_128k_sampled_layers():
+    """The 32-layer 128K workload at full per-layer size, in the launch
+    configuration the benchmark times: layers 0 and 31, decode steps 0 and 127."""
+    cfg = kvsynth.CONFIGS["llama3-8b-128k"]
+    scale = np.float32(1.0 / np.sqrt(cfg.head_dim))
+    for layer in (0, 31):
+        L = kvsynth.make_layer(cfg, layer)
+        for step in (0, 127):
+            q = kvsynth.decode_q(cfg, layer, step, L["channel_scale"])
+            check_all(cfg, L, cfg.keep, q, scale, f"llama3 layer {layer} step {step}")
+
+
+def _custom(seed, lens, **kw):
+    cfg = kvsynth.custom(f"edge{seed}", cfg_id=90, ragged=None, **kw)
+    L = kvsynth.make_layer(cfg, layer=seed)
+    lens = np.asarray(lens, np.int32)
+    for b in range(cfg.batch):
+        L["k_cache"][b, lens[b]:] = kvsynth.nan_value(cfg.dtype)
+        L["v_cache"][b, lens[b]:] = kvsynth.nan_value(cfg.dtype)
+    L["seq_lens"] = lens
+    q = kvsynth.decode_q(cfg, seed, 0, L["channel_scale"])
+    return cfg, L, q
+
+
+EDGE = [
+    # ragged tails, lengths of 1 and not multiples of any tile, odd keep
+    dict(seed=1, lens=[1, 17, 255, 300], batch=4, n_q_heads=8, n_kv_heads=2, head_dim=128,
+         seq_capacity=300, keep=77, dtype="bf16", lowrank=8),
+    dict(seed=2, lens=[1000, 999], batch=2, n_q_heads=4, n_kv_heads=1, head_dim=128,
+         seq_capacity=1001, keep=51, dtype="bf16", lowrank=8),
+    dict(seed=3, lens=[513], batch=1, n_q_heads=16, n_kv_heads=1, head_dim=64, seq_capacity=513,
+         keep=13, dtype="f32"),
+    dict(seed=4, lens=[70, 3], batch=2, n_q_heads=4, n_kv_heads=4, head_dim=8, seq_capacity=77,
+         keep=1, dtype="f32"),
+    dict(seed=5, lens=[129], batch=1, n_q_heads=4, n_kv_heads=2, head_dim=256, seq_capacity=129,
+         keep=256, dtype="bf16"),
+    dict(seed=6, lens=[40], batch=1, n_q_heads=64, n_kv_heads=64, head_dim=256, seq_capacity=40,
+         keep=100, dtype="bf16"),                 # widest row: 64*256*2 = 32 KiB
+    dict(seed=7, lens=[2049, 4096, 1], batch=3, n_q_heads=12, n_kv_heads=3, head_dim=40,
+         seq_capacity=4096, keep=5, dtype="f32"),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[f"edge{c['seed']}" for c in EDGE])
+def test_edge_shapes(case):
+    case = dict(case)
+    seed, lens, keep = case.pop("seed"), case.pop("lens"), case.pop("keep")
+    cfg, L, q = _custom(seed, lens, obs_window=7, keep=keep, **case)
+    check_all(cfg, L, keep, q, np.float32(1.0 / np.sqrt(cfg.head_dim)), f"edge{seed}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_keep_all_reproduces_unpruned_attention(dtype):
+    cfg, L, q = _custom(20, [333, 64], batch=2, n_q_heads=8, n_kv_heads=2, head_dim=64,
+                        seq_capacity=333, keep=64, dtype=dtype, obs_window=5)
+    scale = np.float32(1.0 / 8.0)
+    g = check_all(cfg, L, 64, q, scale, f"keep=D {dtype}")
+    assert (g["idx"] == np.arange(64)).all()
+    full = oracle.full_attn(q, L["k_cache"], L["v_cache"], L["seq_lens"], scale)
+    assert row_rel_err(g["out"], full).max() <= tol_for(dtype)
+
+
+def test_exact_tie_goes_to_lower_channel_and_is_flagged():
+    cfg, L, q = _custom(21, [200], batch=1, n_q_heads=2, n_kv_heads=1, head_dim=32,
+                        seq_capacity=200, keep=16, dtype="bf16", obs_window=4)
+    s = oracle.score(L["k_cache"], L["seq_lens"], L["q_obs"])[0, 0]
+    order = np.lexsort((np.arange(32), -s))
+    a, b = sorted(order[15:17])                 # straddle the cutoff at keep=16
+    for key in ("k_cache", "q_obs"):
+        L[key][..., b] = L[key][..., a]
+    g = check_all(cfg, L, 16, q, np.float32(0.2), "exact tie")
+    assert g["tie"][0, 0] == 1
+    kept = set(g["idx"][0, 0].tolist())
+    assert a in kept and b not in kept
+
+
+def test_zero_length_sequence_gives_zero_scores_and_output():
+    qdk = _qdk()
+    cfg, L, q = _custom(22, [50, 50], batch=2, n_q_heads=2, n_kv_heads=2, head_dim=16,
+                        seq_capacity=50, keep=8, dtype="f32", obs_window=3)
+    lens = np.array([50, 0], np.int32)
+    k, v, qo = to_dev(L["k_cache"]), to_dev(L["v_cache"]), to_dev(L["q_obs"])
+    dl = to_dev(lens)
+    s = qdk.think_score(k, dl, qo)
+    idx, _ = qdk.think_select(s, 8)
+    thin = torch.zeros(2, 50, 2, 8, dtype=k.dtype, device=k.device)
+    qdk.think_compact_k(k, dl, idx, k_thin=thin)
+    out = qdk.think_decode_attn(to_dev(q), thin, v, dl, idx, 0.25)
+    torch.cuda.synchronize()
+    assert (to_host(s)[1] == 0).all()
+    assert (to_host(out)[1] == 0).all()
+    assert (to_host(thin)[1] == 0).all()
