@@ -1,0 +1,301 @@
+#!/usr/bin/env python3
+"""Throughput of the key-channel pruning hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input:
+  for every layer: think_score -> think_select -> think_compact_k
+  then for every decode step and every layer: think_decode_attn
+Default workload: the 32-layer LLaMA-3-8B-like cache, 131072 tokens per
+layer, 32 q / 8 kv heads, head_dim 128, window 64, keep 64 of 128 (bf16),
+score+compact once then 128 decode steps.
+
+Metric: algorithmic HBM bytes moved per second (GB/s), also as a fraction of
+the 8 TB/s peak, and KV tokens per second.  Algorithmic bytes:
+  score+compact, per layer : 2|K| + |K_thin| + |Q_w|   (two streaming reads of K)
+  decode, per call          : |K_thin| + |V| + |q| + |out|
+with |X| counted over valid tokens.  Inputs are resident in HBM before the
+timed region.  Prints one JSON line.
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import kvsynth  # noqa: E402
+
+METRIC = "score+compact and pruned-K decode attn: HBM GB/s, % of peak, KV tokens/s"
+PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="llama3-8b-128k", choices=sorted(kvsynth.CONFIGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=12.0,
+                    help="approximate seconds of oracle work in the CPU baseline sample")
+    return ap.parse_args()
+
+
+def to_dev(a, torch, dev):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(a).to(dev)
+
+
+class Workload:
+    """Device-resident inputs and outputs of every layer, plus pre-marshalled
+    C-ABI arguments so the timed loop does no Python-side checking."""
+
+    def __init__(self, cfg, torch, qdk, dev):
+        self.cfg, self.torch, self.qdk = cfg, torch, qdk
+        B, S, Hq, Hkv, D, keep = (cfg.batch, cfg.seq_capacity, cfg.n_q_heads, cfg.n_kv_heads,
+                                  cfg.head_dim, cfg.keep)
+        tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        self.layers = []
+        t0 = time.time()
+        host0 = None
+        for l in range(cfg.layers):
+            L = kvsynth.make_layer(cfg, l)
+            if l == 0:
+                host0 = L
+            qd = np.stack([kvsynth.decode_q(cfg, l, s, L["channel_scale"])
+                           for s in range(cfg.decode_steps)])
+            ent = dict(k=to_dev(L["k_cache"], torch, dev), v=to_dev(L["v_cache"], torch, dev),
+                       qo=to_dev(L["q_obs"], torch, dev), lens=to_dev(L["seq_lens"], torch, dev),
+                       q=to_dev(qd, torch, dev))
+            ent["scores"] = torch.empty(B, Hkv, D, dtype=torch.float32, device=dev)
+            ent["idx"] = torch.empty(B, Hkv, keep, dtype=torch.int32, device=dev)
+            ent["tie"] = torch.empty(B, Hkv, dtype=torch.int32, device=dev)
+            ent["thin"] = torch.empty(B, S, Hkv, keep, dtype=tdt, device=dev)
+            self.layers.append(ent)
+            if l == 0 or (l + 1) % 8 == 0:
+                log(f"layer {l + 1}/{cfg.layers} resident ({time.time() - t0:.1f}s)")
+            if l > 0:
+                del L
+        self.host0 = host0
+        self.lens_host = host0["seq_lens"]
+        self.out = torch.empty(B, Hq, D, dtype=tdt, device=dev)
+        code = qdk.THINK_BF16 if cfg.dtype == "bf16" else qdk.THINK_F32
+        self.dims = qdk.make_dims(B, Hq, Hkv, D, S, code)
+        self.sel_dims = qdk.make_dims(B, Hkv, Hkv, D, 1, qdk.THINK_F32)
+        self.ws_s = torch.zeros(max(qdk.think_score_workspace_bytes(self.dims), 16),
+                                dtype=torch.uint8, device=dev)
+        self.ws_d = torch.zeros(max(qdk.think_decode_workspace_bytes(self.dims, keep), 16),
+                                dtype=torch.uint8, device=dev)
+        self.scale = ctypes.c_float(1.0 / np.sqrt(D))
+
+    # ---- the path, called through the C ABI with pre-built arguments
+    def score_compact(self, stream):
+        from query_driven_kv_amd import _lib
+        lib, P = _lib.lib, ctypes.c_void_p
+        d, sd, keep = ctypes.byref(self.dims), ctypes.byref(self.sel_dims), self.cfg.keep
+        W = self.cfg.obs_window
+        ws, wsn = P(self.ws_s.data_ptr()), self.ws_s.numel()
+        for e in self.layers:
+            _lib.check("think_score", lib.think_score(
+                d, P(e["k"].data_ptr()), P(e["lens"].data_ptr()), P(e["qo"].data_ptr()), W,
+                P(e["scores"].data_ptr()), ws, wsn, stream))
+            _lib.check("think_select", lib.think_select(
+                sd, P(e["scores"].data_ptr()), keep, P(e["idx"].data_ptr()),
+                P(e["tie"].data_ptr()), stream))
+            _lib.check("think_compact_k", lib.think_compact_k(
+                d, P(e["k"].data_ptr()), P(e["lens"].data_ptr()), P(e["idx"].data_ptr()), keep,
+                P(e["thin"].data_ptr()), stream))
+
+    def prepare_decode(self):
+        P = ctypes.c_void_p
+        self.dec_args = []
+        qstep = self.cfg.batch * self.cfg.n_q_heads * self.cfg.head_dim
+        esz = self.out.element_size()
+        for s in range(self.cfg.decode_steps):
+            row = []
+            for e in self.layers:
+                row.append((P(e["q"].data_ptr() + s * qstep * esz), P(e["thin"].data_ptr()),
+                            P(e["v"].data_ptr()), P(e["lens"].data_ptr()), P(e["idx"].data_ptr())))
+            self.dec_args.append(row)
+
+    def decode(self, stream, steps=None):
+        from query_driven_kv_amd import _lib
+        lib, P = _lib.lib, ctypes.c_void_p
+        d, keep = ctypes.byref(self.dims), self.cfg.keep
+        out, ws, wsn = P(self.out.data_ptr()), P(self.ws_d.data_ptr()), self.ws_d.numel()
+        fn = lib.think_decode_attn
+        for row in self.dec_args[:steps]:
+            for (q, thin, v, lens, idx) in row:
+                rc = fn(d, q, thin, v, lens, idx, keep, self.scale, out, ws, wsn, stream)
+                if rc:
+                    _lib.check("think_decode_attn", rc)
+
+    # ---- algorithmic bytes
+    def bytes_model(self):
+        cfg = self.cfg
+        e = 2 if cfg.dtype == "bf16" else 4
+        tok = int(self.lens_host.sum())
+        K = tok * cfg.n_kv_heads * cfg.head_dim * e
+        Kt = tok * cfg.n_kv_heads * cfg.keep * e
+        Qw = cfg.batch * cfg.obs_window * cfg.n_q_heads * cfg.head_dim * e
+        q = cfg.batch * cfg.n_q_heads * cfg.head_dim * e
+        sc_layer = 2 * K + Kt + Qw
+        dec_call = Kt + K + 2 * q          # |K_thin| + |V| + |q| + |out|  (|V| == |K|)
+        return dict(tokens=tok, sc_layer=sc_layer, dec_call=dec_call,
+                    sc_min_layer=K + Kt + Qw)
+
+
+def cpu_baseline(wl, budget_s):
+    """The oracle, untuned, on a bounded sample of the same workload: full
+    score+select+compact of layer 0, then decode steps of layer 0 until the
+    time budget is spent.  Same algorithmic byte accounting as the GPU."""
+    import oracle
+    cfg, L = wl.cfg, wl.host0
+    bm = wl.bytes_model()
+    threads = oracle.num_threads()
+    t0 = time.perf_counter()
+    s = oracle.score(L["k_cache"], L["seq_lens"], L["q_obs"])
+    idx, _ = oracle.select(s, cfg.keep)
+    thin = oracle.compact(L["k_cache"], L["seq_lens"], idx)
+    t_sc = time.perf_counter() - t0
+    scale = np.float32(1.0 / np.sqrt(cfg.head_dim))
+    steps, t_dec = 0, 0.0
+    while steps < cfg.decode_steps and (t_sc + t_dec < budget_s or steps == 0):
+        q = kvsynth.decode_q(cfg, 0, steps, L["channel_scale"])
+        t1 = time.perf_counter()
+        oracle.decode(q, thin, L["v_cache"], L["seq_lens"], idx, scale)
+        t_dec += time.perf_counter() - t1
+        steps += 1
+    total_bytes = bm["sc_layer"] + steps * bm["dec_call"]
+    total_s = t_sc + t_dec
+    return {"value": round(total_bytes / total_s / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"layer 0 of {cfg.name}: score+select+compact once ({t_sc:.2f}s) and "
+                       f"{steps} decode steps ({t_dec:.2f}s); fp64 C oracle, OpenMP over "
+                       f"(batch, head) pairs, {threads} threads"),
+            "seconds": round(total_s, 2),
+            "score_compact_GBps": round(bm["sc_layer"] / t_sc / 1e9, 4),
+            "decode_GBps": round(steps * bm["dec_call"] / max(t_dec, 1e-9) / 1e9, 4)}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: this path runs on a single MI355X and has no "
+              f"multi-GPU mode (asked for --gpus {args.gpus}, WORLD_SIZE={world}).",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    import query_driven_kv_amd as qdk
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    cfg = kvsynth.CONFIGS[args.workload]
+    log(f"workload {cfg.name}: {cfg.layers} layers, B={cfg.batch}, S={cfg.seq_capacity}, "
+        f"Hq={cfg.n_q_heads}, Hkv={cfg.n_kv_heads}, D={cfg.head_dim}, keep={cfg.keep}, "
+        f"{cfg.decode_steps} decode steps")
+    wl = Workload(cfg, torch, qdk, dev)
+    wl.prepare_decode()
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    bm = wl.bytes_model()
+    n_dec = cfg.decode_steps * cfg.layers
+
+    for _ in range(args.warmup):
+        wl.score_compact(sp)
+        wl.decode(sp)
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        a, b, c = ev[k]
+        a.record(stream)
+        wl.score_compact(sp)
+        b.record(stream)
+        wl.decode(sp)
+        c.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sc_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    dec_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    log(f"timed {args.steps} steps: {wall:.3f}s wall, score+compact {sc_ms:.3f} ms, "
+        f"decode {dec_ms:.3f} ms per step")
+
+    ms_per_step = wall / args.steps * 1e3
+    step_bytes = cfg.layers * bm["sc_layer"] + n_dec * bm["dec_call"]
+    value = step_bytes / (ms_per_step / 1e3) / 1e9
+    tok = bm["tokens"]
+    kv_tok_s = (tok * cfg.layers * (1 + cfg.decode_steps)) / (ms_per_step / 1e3)
+    sc_gbs = cfg.layers * bm["sc_layer"] / (sc_ms / 1e3) / 1e9
+    dec_gbs = n_dec * bm["dec_call"] / (dec_ms / 1e3) / 1e9
+    dec_call_us = dec_ms * 1e3 / n_dec
+    near = int(sum(int(e["tie"].sum().item()) for e in wl.layers))
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded log-normal channel scales, x8 outliers, rank-32 keys + noise)",
+        "config": {"workload": cfg.name, "layers": cfg.layers, "batch": cfg.batch,
+                   "seq_len": cfg.seq_capacity, "n_q_heads": cfg.n_q_heads,
+                   "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim,
+                   "obs_window": cfg.obs_window, "keep": cfg.keep,
+                   "decode_steps": cfg.decode_steps, "valid_tokens_per_layer": tok},
+        "pct_of_peak": round(100 * value / PEAK_GBS, 2),
+        "kv_tokens_per_s": float(f"{kv_tok_s:.4g}"),
+        "paths": {
+            "score_compact": {"ms_per_step": round(sc_ms, 3), "GBps": round(sc_gbs, 1),
+                              "pct_of_peak": round(100 * sc_gbs / PEAK_GBS, 2),
+                              "kv_tokens_per_s": float(f"{tok * cfg.layers / (sc_ms / 1e3):.4g}"),
+                              "bytes_per_layer": bm["sc_layer"],
+                              "single_read_bytes_per_layer": bm["sc_min_layer"]},
+            "decode": {"ms_per_step": round(dec_ms, 3), "GBps": round(dec_gbs, 1),
+                       "pct_of_peak": round(100 * dec_gbs / PEAK_GBS, 2),
+                       "us_per_call": round(dec_call_us, 2),
+                       "kv_tokens_per_s": float(f"{tok * n_dec / (dec_ms / 1e3):.4g}"),
+                       "bytes_per_call": bm["dec_call"]},
+        },
+        "roofline": {"kernel": "think_decode_attn (pruned-K split-K decode)",
+                     "bound": "hbm", "achieved": round(bm["dec_call"] / (dec_call_us * 1e-6) / 1e9, 1),
+                     "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": round(bm["dec_call"] / (dec_call_us * 1e-6) / 1e9 / PEAK_GBS, 4),
+                     "traffic": None,
+                     "timing": (f"HIP events on the launch stream around the {n_dec} decode "
+                                f"launches of each timed step; per-launch mean")},
+        "near_ties": near,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget_s)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

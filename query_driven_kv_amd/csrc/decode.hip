@@ -116,29 +116,55 @@ __global__ __launch_bounds__(kThreads) void k_decode_partial(
     }
 }
 
-// Merge the chunks of one (b, h) in ascending chunk order.
+// Merge the chunks of one (b, h).  The block is D x SG threads: sub-group sg
+// merges a contiguous range of chunks in ascending order with a running
+// maximum, then the SG results are merged in ascending sg order.  Fixed order,
+// so the result is bitwise reproducible.
 template <int DT>
-__global__ __launch_bounds__(256) void k_decode_combine(
+__global__ __launch_bounds__(1024) void k_decode_combine(
         const float* __restrict__ partials, const int32_t* __restrict__ seq_lens, int s_cap,
-        int chunk, int nsplit, int rec, int D, typename Elem<DT>::T* __restrict__ out) {
+        int chunk, int nsplit, int rec, int D, int sg_count, typename Elem<DT>::T* __restrict__ out) {
     using E = Elem<DT>;
     const int h = blockIdx.x, b = blockIdx.y, Hq = gridDim.x;
+    const int tid = threadIdx.x;
+    const int d = tid % D, sg = tid / D;
     const int len = clamp_len(seq_lens, b, s_cap);
     const int ns = (len + chunk - 1) / chunk;
     const float* base = partials + ((size_t)b * Hq + h) * nsplit * rec;
-    for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    const int lo = (int)((int64_t)sg * ns / sg_count), hi = (int)((int64_t)(sg + 1) * ns / sg_count);
+    float M = -INFINITY, L = 0.0f, O = 0.0f;
+    for (int s = lo; s < hi; ++s) {
+        const float* r = base + (size_t)s * rec;
+        const float ms = r[0];
+        if (ms > M) {
+            const float f = expf(M - ms);
+            L *= f;
+            O *= f;
+            M = ms;
+        }
+        const float w = expf(ms - M);
+        L = fmaf(w, r[1], L);
+        O = fmaf(w, r[4 + d], O);
+    }
+    __shared__ float sM[64], sL[64], sO[1024];
+    if (d == 0) {
+        sM[sg] = M;
+        sL[sg] = L;
+    }
+    sO[tid] = O;
+    __syncthreads();
+    if (sg == 0) {
+        float MM = sM[0];
+        for (int r = 1; r < sg_count; ++r) MM = fmaxf(MM, sM[r]);
         float res = 0.0f;
         if (ns > 0) {
-            float M = base[0];
-            for (int s = 1; s < ns; ++s) M = fmaxf(M, base[(size_t)s * rec]);
-            float L = 0.0f, O = 0.0f;
-            for (int s = 0; s < ns; ++s) {
-                const float* r = base + (size_t)s * rec;
-                const float w = expf(r[0] - M);
-                L = fmaf(w, r[1], L);
-                O = fmaf(w, r[4 + d], O);
+            float LL = 0.0f, OO = 0.0f;
+            for (int r = 0; r < sg_count; ++r) {
+                const float f = sL[r] > 0.0f ? expf(sM[r] - MM) : 0.0f;
+                LL = fmaf(f, sL[r], LL);
+                OO = fmaf(f, sO[r * D + d], OO);
             }
-            res = O / L;
+            res = OO / LL;
         }
         E::store(out, ((size_t)b * Hq + h) * D + d, res);
     }
@@ -163,13 +189,15 @@ hipError_t launch_decode(const think_dims& d, const DecodeGeom& g, const void* q
     const int G = d.n_q_heads / d.n_kv_heads;
     dim3 grid(g.nsplit, d.n_kv_heads, d.batch);
     dim3 cgrid(d.n_q_heads, d.batch);
-    const int cthreads = d.head_dim < 256 ? d.head_dim : 256;
+    int sg_count = 1024 / d.head_dim;
+    if (sg_count > 16) sg_count = 16;
+    const int cthreads = d.head_dim * sg_count;
     if (g.mfma) {
         hipError_t e = launch_decode_mfma(d, g, q, k_thin, v_cache, seq_lens, kept_idx, keep,
                                           scale, partials, s);
         if (e != hipSuccess) return e;
         k_decode_combine<THINK_BF16><<<cgrid, cthreads, 0, s>>>(
-            partials, seq_lens, d.seq_capacity, g.chunk, g.nsplit, g.rec, d.head_dim,
+            partials, seq_lens, d.seq_capacity, g.chunk, g.nsplit, g.rec, d.head_dim, sg_count,
             (uint16_t*)out);
     } else if (d.dtype == THINK_BF16) {
         k_decode_partial<THINK_BF16><<<grid, kThreads, 0, s>>>(
@@ -177,14 +205,14 @@ hipError_t launch_decode(const think_dims& d, const DecodeGeom& g, const void* q
             kept_idx, d.seq_capacity, d.n_kv_heads, G, d.head_dim, keep, scale, g.nsplit, g.rec,
             partials);
         k_decode_combine<THINK_BF16><<<cgrid, cthreads, 0, s>>>(
-            partials, seq_lens, d.seq_capacity, g.chunk, g.nsplit, g.rec, d.head_dim,
+            partials, seq_lens, d.seq_capacity, g.chunk, g.nsplit, g.rec, d.head_dim, sg_count,
             (uint16_t*)out);
     } else {
         k_decode_partial<THINK_F32><<<grid, kThreads, 0, s>>>(
             (const float*)q, (const float*)k_thin, (const float*)v_cache, seq_lens, kept_idx,
             d.seq_capacity, d.n_kv_heads, G, d.head_dim, keep, scale, g.nsplit, g.rec, partials);
         k_decode_combine<THINK_F32><<<cgrid, cthreads, 0, s>>>(
-            partials, seq_lens, d.seq_capacity, g.chunk, g.nsplit, g.rec, d.head_dim,
+            partials, seq_lens, d.seq_capacity, g.chunk, g.nsplit, g.rec, d.head_dim, sg_count,
             (float*)out);
     }
     return hipGetLastError();

@@ -1,14 +1,316 @@
-// decode_mfma.hip - bf16 matrix-core decode kernel (not yet enabled).
+// decode_mfma.hip - bf16 matrix-core kernel for stage (d), head_dim 128.
+//
+// "ThinK: Thinner Key Cache by Query-Driven Pruning", Method details ->
+// Technical framework, last step: attention runs on the thinner key cache
+// while the values stay unpruned.  Per (b, q head h), kv = h / G:
+//   l_t = scale * sum_j q[b,h,idx_j] * K_thin[b,t,kv,j],  out = softmax(l) . V[b,:,kv,:]
+//
+// Work decomposition.  Workgroup = (token chunk, kv head, b), 4 waves; each
+// wave walks its quarter of the chunk 32 tokens at a time.  The G <= 16 query
+// heads of the group share every K_thin / V byte the wave loads.
+//
+// Both products run on v_mfma_f32_16x16x32_bf16 (16x16 output, K = 32):
+//   logits  C[t][g] = sum_j K_thin[t][j] * qS[j][g]
+//           A = K_thin rows: lane (l%16 = token, l/16 = channel octet) loads 16
+//               contiguous bytes straight from HBM;  B = gathered query,
+//               loaded once per wave (zero for g >= G or j >= keep).
+//           C lands as lane (l%16 = g, l/16 = token quad, reg = token).
+//   values  O[g][d] = sum_t P[g][t] * V[t][d]
+//           A = P: exactly the registers the logits produced (lane l%16 = g,
+//               8 tokens per lane), rounded to bf16 - no data movement;
+//           B = V: lane (l%16 = d octet, l/16 = token quad) loads the 16-byte
+//               V rows of its 8 tokens; 8 output tiles, tile c taking element c
+//               of each row, re-paired per token with 16-bit permutes.
+// The token order inside one 32-token step is a permutation shared by A and
+// B of the value product, so no transposition through LDS is needed.
+//
+// Online softmax per wave (fp32), the 4 waves merged in LDS, one partial
+// record (m, l, o[128]) per (b, h, chunk) written for the combine kernel.
+// Padding tokens (t >= len_b) are never loaded: their operands are zero and
+// their logits -inf, so a NaN in padding cannot leak in.
 #include "think_common.h"
 
 namespace thinkkv {
+namespace {
 
-bool mfma_decode_supported(const think_dims&, int) { return false; }
-int mfma_decode_chunk(const think_dims&, int) { return 256; }
-hipError_t launch_decode_mfma(const think_dims&, const DecodeGeom&, const void*, const void*,
-                              const void*, const int32_t*, const int32_t*, int, float, float*,
-                              hipStream_t) {
-    return hipErrorNotSupported;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 128;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+
+__device__ __forceinline__ f32x4 mfma(uint4 a, uint4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// 8 consecutive bf16 of a K_thin row; `valid` of them (0..8) are read, the
+// rest are zero.  KAL is the guaranteed element alignment of p (8, 2 or 1).
+template <int KAL>
+__device__ __forceinline__ uint4 load_k8(const uint16_t* p, int valid) {
+    union {
+        uint4 v;
+        uint32_t w[4];
+        uint16_t h[8];
+    } u;
+    u.v = make_uint4(0u, 0u, 0u, 0u);
+    if (KAL == 8) {
+        if (valid > 0) u.v = *reinterpret_cast<const uint4*>(p);
+    } else if (KAL == 2) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (2 * k < valid) u.w[k] = reinterpret_cast<const uint32_t*>(p)[k];
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (k < valid) u.h[k] = p[k];
+    }
+    return u.v;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// Element c (0..7) of each of the 8 V rows of this lane, as one B operand.
+template <int C>
+__device__ __forceinline__ uint4 v_column(const uint4 (&v)[8]) {
+    constexpr int w = C >> 1;
+    uint32_t x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t d = w == 0 ? v[i].x : w == 1 ? v[i].y : w == 2 ? v[i].z : v[i].w;
+        x[i] = d;
+    }
+    uint4 r;
+    if (C & 1) {
+        r.x = (x[0] >> 16) | (x[1] & 0xffff0000u);
+        r.y = (x[2] >> 16) | (x[3] & 0xffff0000u);
+        r.z = (x[4] >> 16) | (x[5] & 0xffff0000u);
+        r.w = (x[6] >> 16) | (x[7] & 0xffff0000u);
+    } else {
+        r.x = (x[0] & 0xffffu) | (x[1] << 16);
+        r.y = (x[2] & 0xffffu) | (x[3] << 16);
+        r.z = (x[4] & 0xffffu) | (x[5] << 16);
+        r.w = (x[6] & 0xffffu) | (x[7] << 16);
+    }
+    return r;
+}
+
+template <int KB, int KAL>
+__global__ __launch_bounds__(kThreads, 2) void k_decode_mfma(
+        const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_thin,
+        const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ seq_lens,
+        const int32_t* __restrict__ kept_idx, int s_cap, int Hkv, int G, int keep, float scale,
+        int chunk, int nsplit, int rec, float* __restrict__ partials) {
+    const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+    const int len = clamp_len(seq_lens, b, s_cap);
+    const int t0 = split * chunk;
+    if (t0 >= len) return;                       // the combine stops before this chunk
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int n16 = lane & 15, q4 = lane >> 4;
+    const int Hq = Hkv * G;
+
+    __shared__ __align__(16) uint16_t s_q[16 * kD];            // gathered query [g][j]
+    __shared__ float s_o[kWaves * 16 * kD];      // per-wave O [w][g][d]
+    __shared__ float s_m[kWaves * 16], s_l[kWaves * 16];
+
+    for (int i = tid; i < 16 * KB * 32; i += kThreads) {
+        const int g = i / (KB * 32), j = i - g * (KB * 32);
+        uint16_t val = 0;
+        if (g < G && j < keep) {
+            int c = kept_idx[((size_t)b * Hkv + kv) * keep + j];
+            c = c < 0 ? 0 : (c >= kD ? kD - 1 : c);
+            val = q[((size_t)b * Hq + kv * G + g) * kD + c];
+        }
+        s_q[g * kD + j] = val;
+    }
+    __syncthreads();
+    uint4 qB[KB];                                // B operand: lane holds qS[jb*32+8*q4+i][g=n16]
+#pragma unroll
+    for (int jb = 0; jb < KB; ++jb)
+        qB[jb] = *reinterpret_cast<const uint4*>(&s_q[n16 * kD + jb * 32 + 8 * q4]);
+
+    const int tw = chunk / kWaves;
+    const int ws = t0 + wave * tw;
+    const int we = min(ws + tw, len);
+    const size_t kt_row = (size_t)Hkv * keep;
+    const uint16_t* kbase = k_thin + (size_t)b * s_cap * kt_row + (size_t)kv * keep;
+    const size_t v_row = (size_t)Hkv * kD;
+    const uint16_t* vbase = v_cache + (size_t)b * s_cap * v_row + (size_t)kv * kD + 8 * n16;
+
+    f32x4 O[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) O[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, l = 0.0f;
+
+    for (int ts = ws; ts < we; ts += 32) {
+        // ---- loads: K_thin A operands (2 token halves x KB channel blocks), V rows
+        uint4 kf[2][KB];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int t = ts + 16 * h + n16;
+#pragma unroll
+            for (int jb = 0; jb < KB; ++jb) {
+                const int j0 = jb * 32 + 8 * q4;
+                int valid = t < we ? keep - j0 : 0;
+                valid = valid < 0 ? 0 : (valid > 8 ? 8 : valid);
+                kf[h][jb] = load_k8<KAL>(kbase + (size_t)t * kt_row + j0, valid);
+            }
+        }
+        uint4 vf[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int t = ts + 4 * q4 + (i & 3) + 16 * (i >> 2);
+            vf[i] = t < we ? *reinterpret_cast<const uint4*>(vbase + (size_t)t * v_row)
+                           : make_uint4(0u, 0u, 0u, 0u);
+        }
+        // ---- logits of 32 tokens x 16 heads
+        f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int jb = 0; jb < KB; ++jb) {
+            c0 = mfma(kf[0][jb], qB[jb], c0);
+            c1 = mfma(kf[1][jb], qB[jb], c1);
+        }
+        float x[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            x[r] = ts + 4 * q4 + r < we ? c0[r] * scale : -INFINITY;
+            x[4 + r] = ts + 16 + 4 * q4 + r < we ? c1[r] * scale : -INFINITY;
+        }
+        // ---- online softmax for head g = n16 (token ts is valid, so mx is finite)
+        float mx = x[0];
+#pragma unroll
+        for (int r = 1; r < 8; ++r) mx = fmaxf(mx, x[r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mn = fmaxf(m, mx);
+        const float alpha = expf(m - mn);
+        uint32_t pw[4];
+        float ps = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float p0 = expf(x[2 * r] - mn), p1 = expf(x[2 * r + 1] - mn);
+            pw[r] = pack_bf16(p0, p1);
+            ps += bf16_lo(pw[r]) + bf16_hi(pw[r]);   // sum what the product will use
+        }
+        ps += __shfl_xor(ps, 16);
+        ps += __shfl_xor(ps, 32);
+        l = l * alpha + ps;
+        m = mn;
+        // O rows are g = 4*q4 + i: fetch those heads' rescale factors
+        float aO[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) aO[i] = __shfl(alpha, 4 * q4 + i);
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) O[c][i] *= aO[i];
+        // ---- values: A = P (k slot 8*q4+i <-> token ts + 4*q4 + (i&3) + 16*(i>>2))
+        const uint4 pa = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+        O[0] = mfma(pa, v_column<0>(vf), O[0]);
+        O[1] = mfma(pa, v_column<1>(vf), O[1]);
+        O[2] = mfma(pa, v_column<2>(vf), O[2]);
+        O[3] = mfma(pa, v_column<3>(vf), O[3]);
+        O[4] = mfma(pa, v_column<4>(vf), O[4]);
+        O[5] = mfma(pa, v_column<5>(vf), O[5]);
+        O[6] = mfma(pa, v_column<6>(vf), O[6]);
+        O[7] = mfma(pa, v_column<7>(vf), O[7]);
+    }
+
+    // ---- merge the 4 waves (a wave past len_b has m = -inf, l = 0, O = 0)
+    if (q4 == 0) {
+        s_m[wave * 16 + n16] = m;
+        s_l[wave * 16 + n16] = l;
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int g = 4 * q4 + i;
+            if (g < G) s_o[(wave * 16 + g) * kD + 8 * n16 + c] = O[c][i];
+        }
+    __syncthreads();
+    for (int e = tid; e < G * kD; e += kThreads) {
+        const int g = e / kD, d = e - g * kD;
+        float M = s_m[g];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w * 16 + g]);
+        float L = 0.0f, o = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float f = expf(s_m[w * 16 + g] - M);
+            L = fmaf(f, s_l[w * 16 + g], L);
+            o = fmaf(f, s_o[(w * 16 + g) * kD + d], o);
+        }
+        float* r = partials + (((size_t)b * Hq + kv * G + g) * nsplit + split) * rec;
+        r[4 + d] = o;
+        if (d == 0) {
+            r[0] = M;
+            r[1] = L;
+        }
+    }
+}
+
+template <int KB>
+hipError_t launch_kb(int kal, dim3 grid, hipStream_t s, const uint16_t* q, const uint16_t* kt,
+                     const uint16_t* v, const int32_t* lens, const int32_t* idx, int s_cap,
+                     int Hkv, int G, int keep, float scale, int chunk, int nsplit, int rec,
+                     float* part) {
+    if (kal == 8)
+        k_decode_mfma<KB, 8><<<grid, kThreads, 0, s>>>(q, kt, v, lens, idx, s_cap, Hkv, G, keep,
+                                                       scale, chunk, nsplit, rec, part);
+    else if (kal == 2)
+        k_decode_mfma<KB, 2><<<grid, kThreads, 0, s>>>(q, kt, v, lens, idx, s_cap, Hkv, G, keep,
+                                                       scale, chunk, nsplit, rec, part);
+    else
+        k_decode_mfma<KB, 1><<<grid, kThreads, 0, s>>>(q, kt, v, lens, idx, s_cap, Hkv, G, keep,
+                                                       scale, chunk, nsplit, rec, part);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool mfma_decode_supported(const think_dims& d, int keep) {
+    return d.dtype == THINK_BF16 && d.head_dim == kD && d.n_q_heads / d.n_kv_heads <= 16 &&
+           keep >= 1 && keep <= kD;
+}
+
+// Tokens per workgroup: a multiple of 128 (one 32-token step per wave), sized
+// for about 512 workgroups (two per CU) so the combine stays small.
+int mfma_decode_chunk(const think_dims& d, int keep) {
+    (void)keep;
+    const int64_t work = (int64_t)d.seq_capacity * d.n_kv_heads * d.batch;
+    int64_t chunk = (work + 511) / 512;
+    chunk = (chunk + 127) / 128 * 128;
+    if (chunk < 128) chunk = 128;
+    if (chunk > 8192) chunk = 8192;
+    return (int)chunk;
+}
+
+hipError_t launch_decode_mfma(const think_dims& d, const DecodeGeom& g, const void* q,
+                              const void* k_thin, const void* v_cache, const int32_t* seq_lens,
+                              const int32_t* kept_idx, int keep, float scale, float* partials,
+                              hipStream_t s) {
+    const int G = d.n_q_heads / d.n_kv_heads;
+    const int kal = keep % 8 == 0 ? 8 : (keep % 2 == 0 ? 2 : 1);
+    const int KB = (keep + 31) / 32;
+    dim3 grid(g.nsplit, d.n_kv_heads, d.batch);
+    auto qp = (const uint16_t*)q;
+    auto kp = (const uint16_t*)k_thin;
+    auto vp = (const uint16_t*)v_cache;
+    switch (KB) {
+        case 1: return launch_kb<1>(kal, grid, s, qp, kp, vp, seq_lens, kept_idx, d.seq_capacity,
+                                    d.n_kv_heads, G, keep, scale, g.chunk, g.nsplit, g.rec, partials);
+        case 2: return launch_kb<2>(kal, grid, s, qp, kp, vp, seq_lens, kept_idx, d.seq_capacity,
+                                    d.n_kv_heads, G, keep, scale, g.chunk, g.nsplit, g.rec, partials);
+        case 3: return launch_kb<3>(kal, grid, s, qp, kp, vp, seq_lens, kept_idx, d.seq_capacity,
+                                    d.n_kv_heads, G, keep, scale, g.chunk, g.nsplit, g.rec, partials);
+        default: return launch_kb<4>(kal, grid, s, qp, kp, vp, seq_lens, kept_idx, d.seq_capacity,
+                                     d.n_kv_heads, G, keep, scale, g.chunk, g.nsplit, g.rec, partials);
+    }
 }
 
 }  // namespace thinkkv

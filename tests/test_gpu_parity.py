@@ -137,6 +137,16 @@ EDGE = [
          keep=100, dtype="bf16"),                 # widest row: 64*256*2 = 32 KiB
     dict(seed=7, lens=[2049, 4096, 1], batch=3, n_q_heads=12, n_kv_heads=3, head_dim=40,
          seq_capacity=4096, keep=5, dtype="f32"),
+    # head_dim 128 bf16 (matrix-core kernel): even keep not a multiple of 8, every
+    # channel kept, a single channel kept, groups of 8 and 16 query heads
+    dict(seed=8, lens=[777, 1], batch=2, n_q_heads=16, n_kv_heads=2, head_dim=128,
+         seq_capacity=800, keep=42, dtype="bf16", lowrank=16),
+    dict(seed=9, lens=[300], batch=1, n_q_heads=16, n_kv_heads=1, head_dim=128,
+         seq_capacity=300, keep=128, dtype="bf16"),
+    dict(seed=10, lens=[129, 64, 1000], batch=3, n_q_heads=3, n_kv_heads=3, head_dim=128,
+         seq_capacity=1000, keep=1, dtype="bf16"),
+    dict(seed=11, lens=[5000, 2500], batch=2, n_q_heads=32, n_kv_heads=4, head_dim=128,
+         seq_capacity=5000, keep=96, dtype="bf16", lowrank=32),
 ]
 
 
