@@ -71,7 +71,7 @@ typedef struct {
     int32_t dtype;        /* think_dtype of K, V, Q_w, q, K_thin and out */
 } think_dims;
 /* Further limits (THINK_ERR_UNSUPPORTED): B <= 65535, Hq/Hkv <= 16,
- * Hkv*D*element_size <= 32 KiB, S_cap <= 2^28. */
+ * Hkv*D*element_size <= 32 KiB, S_cap <= 2^28, B*S_cap < 2^31. */
 
 /* Version of this ABI (THINK_ABI_VERSION of the built library). */
 THINK_API int think_abi_version(void);
@@ -145,7 +145,9 @@ THINK_API int think_compact_k(const think_dims *d, const void *k_cache, const in
  * Values are not pruned.  The caller passes softmax_scale (1/sqrt(D) with the
  * unpruned D reproduces unpruned attention at keep == D).
  *   q         [B,Hq,D] dtype           out  [B,Hq,D] dtype (written)
- *   workspace >= think_decode_workspace_bytes(d, keep), 16-byte aligned.
+ *   workspace >= think_decode_workspace_bytes(d, keep), 16-byte aligned,
+ *             caller-owned scratch (per-chunk partial softmax records); calls
+ *             sharing one workspace must be ordered (same stream).
  * Precision: fp32 accumulation (bf16 matrix-core products for bf16 inputs);
  * per row ||out - exact||_inf / ||exact||_inf <= 1e-5 (fp32), 2e-2 (bf16).
  */

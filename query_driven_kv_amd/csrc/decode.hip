@@ -14,9 +14,9 @@
 // (running max m, sum l, unnormalised o[D]) to the workspace; a combine
 // kernel merges the chunks of each (b, h) in ascending chunk order.
 //
-// This file holds the general kernel (any dtype, any keep, G <= 16).  The
-// bf16 matrix-core kernel for the bandwidth-critical shapes is in
-// decode_mfma.hip and writes the same partial records.
+// This file holds the general kernel (any dtype, any keep, G <= 16) and the
+// combine kernel.  The bf16 matrix-core kernel for the bandwidth-critical
+// shapes is in decode_mfma.hip and writes the same partial records.
 #include "think_common.h"
 
 namespace thinkkv {
@@ -117,8 +117,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_partial(
 }
 
 // Merge the chunks of one (b, h).  The block is D x SG threads: sub-group sg
-// merges a contiguous range of chunks in ascending order with a running
-// maximum, then the SG results are merged in ascending sg order.  Fixed order,
+// merges a contiguous range of chunks in ascending order, eight at a time
+// with a running maximum, then the SG results are merged in ascending sg order.  Fixed order,
 // so the result is bitwise reproducible.
 template <int DT>
 __global__ __launch_bounds__(1024) void k_decode_combine(
@@ -132,19 +132,38 @@ __global__ __launch_bounds__(1024) void k_decode_combine(
     const int ns = (len + chunk - 1) / chunk;
     const float* base = partials + ((size_t)b * Hq + h) * nsplit * rec;
     const int lo = (int)((int64_t)sg * ns / sg_count), hi = (int)((int64_t)(sg + 1) * ns / sg_count);
+    // records are loaded eight at a time before they are merged, so their
+    // loads overlap instead of each waiting on the previous merge step
     float M = -INFINITY, L = 0.0f, O = 0.0f;
-    for (int s = lo; s < hi; ++s) {
-        const float* r = base + (size_t)s * rec;
-        const float ms = r[0];
-        if (ms > M) {
-            const float f = expf(M - ms);
-            L *= f;
-            O *= f;
-            M = ms;
+    for (int s0 = lo; s0 < hi; s0 += 8) {
+        float mv[8], lv[8], ov[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int s = s0 + k;
+            if (s < hi) {
+                const float* r = base + (size_t)s * rec;
+                mv[k] = r[0];
+                lv[k] = r[1];
+                ov[k] = r[4 + d];
+            } else {
+                mv[k] = -INFINITY;
+                lv[k] = 0.0f;
+                ov[k] = 0.0f;
+            }
         }
-        const float w = expf(ms - M);
-        L = fmaf(w, r[1], L);
-        O = fmaf(w, r[4 + d], O);
+        float Mn = M;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) Mn = fmaxf(Mn, mv[k]);
+        const float f = expf(M - Mn);            // M = -inf on the first batch: f = 0
+        L *= f;
+        O *= f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float w = expf(mv[k] - Mn);
+            L = fmaf(w, lv[k], L);
+            O = fmaf(w, ov[k], O);
+        }
+        M = Mn;
     }
     __shared__ float sM[64], sL[64], sO[1024];
     if (d == 0) {
@@ -185,7 +204,8 @@ DecodeGeom decode_geom(const think_dims& d, int keep) {
 hipError_t launch_decode(const think_dims& d, const DecodeGeom& g, const void* q,
                          const void* k_thin, const void* v_cache, const int32_t* seq_lens,
                          const int32_t* kept_idx, int keep, float scale, void* out,
-                         float* partials, hipStream_t s) {
+                         void* workspace, hipStream_t s) {
+    float* partials = reinterpret_cast<float*>(workspace);
     const int G = d.n_q_heads / d.n_kv_heads;
     dim3 grid(g.nsplit, d.n_kv_heads, d.batch);
     dim3 cgrid(d.n_q_heads, d.batch);

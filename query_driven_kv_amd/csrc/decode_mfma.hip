@@ -25,9 +25,15 @@
 // B of the value product, so no transposition through LDS is needed.
 //
 // Online softmax per wave (fp32), the 4 waves merged in LDS, one partial
-// record (m, l, o[128]) per (b, h, chunk) written for the combine kernel.
-// Padding tokens (t >= len_b) are never loaded: their operands are zero and
-// their logits -inf, so a NaN in padding cannot leak in.
+// record (m, l, o[128]) per (b, h, chunk) for the combine kernel.  (Merging
+// in the last-finishing workgroup instead needs a device-scope release per
+// workgroup, an L2 write-back on this part, which costs more than the
+// second launch.)  K_thin and V are read once per call: the loads are marked
+// non-temporal.
+// Loads are raw buffer loads whose per-step descriptors end at the last
+// valid token: padding tokens (t >= len_b) read as zero and their logits are
+// set to -inf, so a NaN in padding cannot leak in; no load sits behind a
+// branch.
 #include "think_common.h"
 
 namespace thinkkv {
@@ -45,28 +51,42 @@ __device__ __forceinline__ f32x4 mfma(uint4 a, uint4 b, f32x4 c) {
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// 8 consecutive bf16 of a K_thin row; `valid` of them (0..8) are read, the
-// rest are zero.  KAL is the guaranteed element alignment of p (8, 2 or 1).
+// Buffer loads: a wave-uniform descriptor (base, size in bytes) lives in
+// SGPRs and each lane supplies a 32-bit byte offset.  An offset at or past
+// the size reads as zero in hardware, which is how tokens past the valid
+// range and channels past `keep` are masked without branches.
+constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, 32-bit data format
+constexpr int kNonTemporal = 2;                 // streaming: read once per call
+constexpr uint32_t kOff = 0x80000000u;          // an offset past any descriptor
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             kRsrcWord3);
+}
+
+// 8 consecutive bf16 of a K_thin head row at byte offset `off` (kOff: none).
+// `mask` zeroes the channels past keep inside the last octet of a row when
+// rows are not 16-byte aligned (KAL = 2 or 1: dword or element loads).
 template <int KAL>
-__device__ __forceinline__ uint4 load_k8(const uint16_t* p, int valid) {
-    union {
-        uint4 v;
-        uint32_t w[4];
-        uint16_t h[8];
-    } u;
-    u.v = make_uint4(0u, 0u, 0u, 0u);
+__device__ __forceinline__ uint4 load_k8(__amdgpu_buffer_rsrc_t r, uint32_t off, const uint4& mask) {
     if (KAL == 8) {
-        if (valid > 0) u.v = *reinterpret_cast<const uint4*>(p);
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kNonTemporal);
+        return make_uint4(v.x, v.y, v.z, v.w);
     } else if (KAL == 2) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            if (2 * k < valid) u.w[k] = reinterpret_cast<const uint32_t*>(p)[k];
+        uint4 v;
+        v.x = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kNonTemporal) & mask.x;
+        v.y = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(off + 4), 0, kNonTemporal) & mask.y;
+        v.z = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(off + 8), 0, kNonTemporal) & mask.z;
+        v.w = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(off + 12), 0, kNonTemporal) & mask.w;
+        return v;
     } else {
+        uint32_t h[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-            if (k < valid) u.h[k] = p[k];
+            h[k] = __builtin_amdgcn_raw_buffer_load_b16(r, (int)(off + 2 * k), 0, kNonTemporal);
+        return make_uint4((h[0] | (h[1] << 16)) & mask.x, (h[2] | (h[3] << 16)) & mask.y,
+                          (h[4] | (h[5] << 16)) & mask.z, (h[6] | (h[7] << 16)) & mask.w);
     }
-    return u.v;
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
@@ -98,6 +118,120 @@ __device__ __forceinline__ uint4 v_column(const uint4 (&v)[8]) {
     return r;
 }
 
+template <int KB>
+struct Frag {
+    uint4 k[2][KB];   // K_thin A operands: token half x 32-channel block
+    uint4 v[8];       // V rows of this lane's 8 tokens (16 bytes each)
+};
+
+// Lane-constant parts of the loads of one 32-token step (byte offsets from
+// the step's first K_thin / V row of this kv head).
+template <int KB>
+struct LaneOffsets {
+    uint32_t k[2][KB];   // K_thin octet [half][channel block]; kOff when past keep
+    uint4 kmask[KB];     // channel mask of the octet (KAL 2 / 1)
+    uint32_t v[8];       // V row of this lane's token i, channel octet n16
+};
+
+template <int KB>
+__device__ __forceinline__ LaneOffsets<KB> lane_offsets(int keep, size_t kt_row, size_t v_row,
+                                                        int n16, int q4) {
+    LaneOffsets<KB> lo;
+#pragma unroll
+    for (int jb = 0; jb < KB; ++jb) {
+        const int j0 = jb * 32 + 8 * q4;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            lo.k[h][jb] = j0 < keep ? (uint32_t)(((16 * h + n16) * kt_row + j0) * 2) : kOff;
+        uint32_t mw[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int j = j0 + 2 * w;
+            mw[w] = (j < keep ? 0x0000ffffu : 0u) | (j + 1 < keep ? 0xffff0000u : 0u);
+        }
+        lo.kmask[jb] = make_uint4(mw[0], mw[1], mw[2], mw[3]);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        lo.v[i] = (uint32_t)(((4 * q4 + (i & 3) + 16 * (i >> 2)) * v_row + 8 * n16) * 2);
+    return lo;
+}
+
+// Issue the loads of one 32-token step: rk / rv cover this kv head's rows of
+// the step's valid tokens only, so every other read returns zero.
+template <int KB, int KAL>
+__device__ __forceinline__ void load_step(Frag<KB>& f, __amdgpu_buffer_rsrc_t rk,
+                                          __amdgpu_buffer_rsrc_t rv, const LaneOffsets<KB>& lo) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int jb = 0; jb < KB; ++jb) f.k[h][jb] = load_k8<KAL>(rk, lo.k[h][jb], lo.kmask[jb]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)lo.v[i], 0, kNonTemporal);
+        f.v[i] = make_uint4(x.x, x.y, x.z, x.w);
+    }
+}
+
+// Logits, online softmax and the value product of one 32-token step.
+template <int KB>
+__device__ __forceinline__ void compute_step(const Frag<KB>& f, int nt, float scale,
+                                             const uint4 (&qB)[KB], int q4, f32x4 (&O)[8],
+                                             float& m, float& l) {
+    f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jb = 0; jb < KB; ++jb) {
+        c0 = mfma(f.k[0][jb], qB[jb], c0);
+        c1 = mfma(f.k[1][jb], qB[jb], c1);
+    }
+    // c0[r]: token 4*q4 + r of the step, c1[r]: token 16 + 4*q4 + r (nt of
+    // the 32 are valid); head g = lane % 16
+    float x[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        x[r] = 4 * q4 + r < nt ? c0[r] * scale : -INFINITY;
+        x[4 + r] = 16 + 4 * q4 + r < nt ? c1[r] * scale : -INFINITY;
+    }
+    // online softmax for head g (the step's first token is valid: mx is finite)
+    float mx = x[0];
+#pragma unroll
+    for (int r = 1; r < 8; ++r) mx = fmaxf(mx, x[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(m, mx);
+    const float alpha = expf(m - mn);
+    uint32_t pw[4];
+    float ps = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float p0 = expf(x[2 * r] - mn), p1 = expf(x[2 * r + 1] - mn);
+        pw[r] = pack_bf16(p0, p1);
+        ps += bf16_lo(pw[r]) + bf16_hi(pw[r]);   // sum what the value product uses
+    }
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    l = l * alpha + ps;
+    m = mn;
+    // O rows are heads g = 4*q4 + i: fetch those heads' rescale factors
+    float aO[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) aO[i] = __shfl(alpha, 4 * q4 + i);
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[c][i] *= aO[i];
+    // values: A = P (k slot 8*q4+i <-> token ts + 4*q4 + (i&3) + 16*(i>>2))
+    const uint4 pa = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+    O[0] = mfma(pa, v_column<0>(f.v), O[0]);
+    O[1] = mfma(pa, v_column<1>(f.v), O[1]);
+    O[2] = mfma(pa, v_column<2>(f.v), O[2]);
+    O[3] = mfma(pa, v_column<3>(f.v), O[3]);
+    O[4] = mfma(pa, v_column<4>(f.v), O[4]);
+    O[5] = mfma(pa, v_column<5>(f.v), O[5]);
+    O[6] = mfma(pa, v_column<6>(f.v), O[6]);
+    O[7] = mfma(pa, v_column<7>(f.v), O[7]);
+}
+
 template <int KB, int KAL>
 __global__ __launch_bounds__(kThreads, 2) void k_decode_mfma(
         const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_thin,
@@ -107,11 +241,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode_mfma(
     const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
     const int len = clamp_len(seq_lens, b, s_cap);
     const int t0 = split * chunk;
-    if (t0 >= len) return;                       // the combine stops before this chunk
     const int tid = threadIdx.x;
+    const int Hq = Hkv * G;
+    if (t0 >= len) return;                       // the combine stops before this chunk
     const int lane = tid & 63, wave = tid >> 6;
     const int n16 = lane & 15, q4 = lane >> 4;
-    const int Hq = Hkv * G;
 
     __shared__ __align__(16) uint16_t s_q[16 * kD];            // gathered query [g][j]
     __shared__ float s_o[kWaves * 16 * kD];      // per-wave O [w][g][d]
@@ -134,90 +268,58 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode_mfma(
         qB[jb] = *reinterpret_cast<const uint4*>(&s_q[n16 * kD + jb * 32 + 8 * q4]);
 
     const int tw = chunk / kWaves;
-    const int ws = t0 + wave * tw;
+    const int ws = t0 + __builtin_amdgcn_readfirstlane(wave) * tw;   // wave-uniform
     const int we = min(ws + tw, len);
     const size_t kt_row = (size_t)Hkv * keep;
-    const uint16_t* kbase = k_thin + (size_t)b * s_cap * kt_row + (size_t)kv * keep;
     const size_t v_row = (size_t)Hkv * kD;
-    const uint16_t* vbase = v_cache + (size_t)b * s_cap * v_row + (size_t)kv * kD + 8 * n16;
+    const LaneOffsets<KB> lo = lane_offsets<KB>(keep, kt_row, v_row, n16, q4);
+    // this wave's first rows of kv head kv; the valid bytes of a step starting
+    // at token ts end at the last valid token's row
+    const uint16_t* kw = k_thin + ((size_t)b * s_cap + ws) * kt_row + (size_t)kv * keep;
+    const uint16_t* vw = v_cache + ((size_t)b * s_cap + ws) * v_row + (size_t)kv * kD;
+    // descriptors of the step starting at token ts: empty once ts >= we
+    auto rsrc_k = [&](int ts) {
+        const int nt = min(32, we - ts);
+        const uint32_t bytes = nt > 0 ? (uint32_t)(((nt - 1) * kt_row + keep) * 2) : 0u;
+        return make_rsrc(kw + (size_t)(ts - ws) * kt_row, bytes);
+    };
+    auto rsrc_v = [&](int ts) {
+        const int nt = min(32, we - ts);
+        const uint32_t bytes = nt > 0 ? (uint32_t)(((nt - 1) * v_row + kD) * 2) : 0u;
+        return make_rsrc(vw + (size_t)(ts - ws) * v_row, bytes);
+    };
 
     f32x4 O[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) O[c] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, l = 0.0f;
 
-    for (int ts = ws; ts < we; ts += 32) {
-        // ---- loads: K_thin A operands (2 token halves x KB channel blocks), V rows
-        uint4 kf[2][KB];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int t = ts + 16 * h + n16;
-#pragma unroll
-            for (int jb = 0; jb < KB; ++jb) {
-                const int j0 = jb * 32 + 8 * q4;
-                int valid = t < we ? keep - j0 : 0;
-                valid = valid < 0 ? 0 : (valid > 8 ? 8 : valid);
-                kf[h][jb] = load_k8<KAL>(kbase + (size_t)t * kt_row + j0, valid);
+    // Two fragment buffers: the loads of step s+1 are in flight while step s
+    // computes.  Both buffers are loaded unconditionally (a step past the end
+    // has an empty descriptor and reads zeros without touching memory), so
+    // the wait before each compute covers only that buffer's own loads.
+    // (Rows that are not 4-byte aligned are read element by element; with
+    // three or more channel blocks a second buffer would not fit in
+    // registers, so those shapes use one.)
+    constexpr bool kTwoBuffers = KAL == 8 || KB <= 2 || (KAL == 2 && KB <= 3);
+    Frag<KB> fa;
+    if (ws < we) {
+        if constexpr (kTwoBuffers) {
+            Frag<KB> fb;
+            load_step<KB, KAL>(fa, rsrc_k(ws), rsrc_v(ws), lo);
+            for (int ts = ws; ts < we; ts += 64) {
+                load_step<KB, KAL>(fb, rsrc_k(ts + 32), rsrc_v(ts + 32), lo);
+                compute_step<KB>(fa, min(32, we - ts), scale, qB, q4, O, m, l);
+                load_step<KB, KAL>(fa, rsrc_k(ts + 64), rsrc_v(ts + 64), lo);
+                if (ts + 32 < we)
+                    compute_step<KB>(fb, min(32, we - ts - 32), scale, qB, q4, O, m, l);
+            }
+        } else {
+            for (int ts = ws; ts < we; ts += 32) {
+                load_step<KB, KAL>(fa, rsrc_k(ts), rsrc_v(ts), lo);
+                compute_step<KB>(fa, min(32, we - ts), scale, qB, q4, O, m, l);
             }
         }
-        uint4 vf[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int t = ts + 4 * q4 + (i & 3) + 16 * (i >> 2);
-            vf[i] = t < we ? *reinterpret_cast<const uint4*>(vbase + (size_t)t * v_row)
-                           : make_uint4(0u, 0u, 0u, 0u);
-        }
-        // ---- logits of 32 tokens x 16 heads
-        f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int jb = 0; jb < KB; ++jb) {
-            c0 = mfma(kf[0][jb], qB[jb], c0);
-            c1 = mfma(kf[1][jb], qB[jb], c1);
-        }
-        float x[8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            x[r] = ts + 4 * q4 + r < we ? c0[r] * scale : -INFINITY;
-            x[4 + r] = ts + 16 + 4 * q4 + r < we ? c1[r] * scale : -INFINITY;
-        }
-        // ---- online softmax for head g = n16 (token ts is valid, so mx is finite)
-        float mx = x[0];
-#pragma unroll
-        for (int r = 1; r < 8; ++r) mx = fmaxf(mx, x[r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mn = fmaxf(m, mx);
-        const float alpha = expf(m - mn);
-        uint32_t pw[4];
-        float ps = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float p0 = expf(x[2 * r] - mn), p1 = expf(x[2 * r + 1] - mn);
-            pw[r] = pack_bf16(p0, p1);
-            ps += bf16_lo(pw[r]) + bf16_hi(pw[r]);   // sum what the product will use
-        }
-        ps += __shfl_xor(ps, 16);
-        ps += __shfl_xor(ps, 32);
-        l = l * alpha + ps;
-        m = mn;
-        // O rows are g = 4*q4 + i: fetch those heads' rescale factors
-        float aO[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) aO[i] = __shfl(alpha, 4 * q4 + i);
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) O[c][i] *= aO[i];
-        // ---- values: A = P (k slot 8*q4+i <-> token ts + 4*q4 + (i&3) + 16*(i>>2))
-        const uint4 pa = make_uint4(pw[0], pw[1], pw[2], pw[3]);
-        O[0] = mfma(pa, v_column<0>(vf), O[0]);
-        O[1] = mfma(pa, v_column<1>(vf), O[1]);
-        O[2] = mfma(pa, v_column<2>(vf), O[2]);
-        O[3] = mfma(pa, v_column<3>(vf), O[3]);
-        O[4] = mfma(pa, v_column<4>(vf), O[4]);
-        O[5] = mfma(pa, v_column<5>(vf), O[5]);
-        O[6] = mfma(pa, v_column<6>(vf), O[6]);
-        O[7] = mfma(pa, v_column<7>(vf), O[7]);
     }
 
     // ---- merge the 4 waves (a wave past len_b has m = -inf, l = 0, O = 0)
@@ -252,6 +354,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode_mfma(
             r[1] = L;
         }
     }
+
 }
 
 template <int KB>
@@ -279,14 +382,15 @@ bool mfma_decode_supported(const think_dims& d, int keep) {
 }
 
 // Tokens per workgroup: a multiple of 128 (one 32-token step per wave), sized
-// for about 512 workgroups (two per CU) so the combine stays small.
+// for about 512 workgroups (two per CU) and at most 256 chunks per sequence.
 int mfma_decode_chunk(const think_dims& d, int keep) {
     (void)keep;
     const int64_t work = (int64_t)d.seq_capacity * d.n_kv_heads * d.batch;
     int64_t chunk = (work + 511) / 512;
+    const int64_t min_chunk = ((int64_t)d.seq_capacity + 255) / 256;
+    if (chunk < min_chunk) chunk = min_chunk;
     chunk = (chunk + 127) / 128 * 128;
     if (chunk < 128) chunk = 128;
-    if (chunk > 8192) chunk = 8192;
     return (int)chunk;
 }
 

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(kThreads) void k_score_partial(
 #pragma unroll
             for (int u = 0; u < kRun; ++u) {
                 const int tt = t + u * rpi;
-                v[u] = tt < t1 ? base[(size_t)tt * nvec] : make_uint4(0u, 0u, 0u, 0u);
+                v[u] = tt < t1 ? ldg_stream(base + (size_t)tt * nvec) : make_uint4(0u, 0u, 0u, 0u);
             }
             float run[EPV];
 #pragma unroll
@@ -103,12 +103,19 @@ __global__ __launch_bounds__(1024) void k_score_finalize(
     const int ns = (len + tpw - 1) / tpw;
     const int R = Hkv * D;
 
-    // split range of this sub-group, ascending
-    const int lo = (int)((int64_t)sg * ns / sg_count);
-    const int hi = (int)((int64_t)(sg + 1) * ns / sg_count);
-    double k2 = 0.0;
+    // Sub-group sg sums splits sg, sg+SG, sg+2SG, ... into four interleaved
+    // fp64 accumulators (independent loads), combined in a fixed order.
     const float* p = partials + (size_t)b * nsplit * R + (size_t)kv * D + c;
-    for (int s = lo; s < hi; ++s) k2 += (double)p[(size_t)s * R];
+    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+    int s = sg;
+    for (; s + 3 * sg_count < ns; s += 4 * sg_count) {
+        a0 += (double)p[(size_t)s * R];
+        a1 += (double)p[(size_t)(s + sg_count) * R];
+        a2 += (double)p[(size_t)(s + 2 * sg_count) * R];
+        a3 += (double)p[(size_t)(s + 3 * sg_count) * R];
+    }
+    for (; s < ns; s += sg_count) a0 += (double)p[(size_t)s * R];
+    const double k2 = (a0 + a1) + (a2 + a3);
 
     __shared__ double kred[1024];
     __shared__ double qn[16 * 256];
@@ -139,9 +146,9 @@ ScoreGeom score_geom(const think_dims& d) {
     const int e = elem_bytes(d.dtype);
     g.nvec = d.n_kv_heads * d.head_dim * e / 16;
     g.ncg = (g.nvec + kThreads - 1) / kThreads;
-    // aim for ~1024 workgroups; tokens per workgroup a multiple of 16
+    // aim for ~512 workgroups (two per CU); tokens per workgroup a multiple of 16
     const int64_t rows = (int64_t)d.seq_capacity * d.batch * g.ncg;
-    int64_t tpw = (rows + 1023) / 1024;
+    int64_t tpw = (rows + 511) / 512;
     tpw = (tpw + 15) / 16 * 16;
     if (tpw < 16) tpw = 16;
     if (tpw > 4096) tpw = 4096;

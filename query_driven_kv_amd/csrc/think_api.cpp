@@ -23,6 +23,7 @@ int check_dims(const think_dims* d) {
     if ((int64_t)d->n_kv_heads * d->head_dim * thinkkv::elem_bytes(d->dtype) > 32768)
         return THINK_ERR_UNSUPPORTED;
     if (d->seq_capacity > (1 << 28)) return THINK_ERR_UNSUPPORTED;
+    if ((int64_t)d->batch * d->seq_capacity > INT32_MAX) return THINK_ERR_UNSUPPORTED;
     return THINK_OK;
 }
 
@@ -110,8 +111,7 @@ int think_decode_attn(const think_dims* d, const void* q, const void* k_thin,
     if (!workspace || workspace_bytes < g.ws_bytes || !aligned16(workspace))
         return THINK_ERR_WORKSPACE;
     return hip_status(thinkkv::launch_decode(*d, g, q, k_thin, v_cache, seq_lens, kept_idx, keep,
-                                             softmax_scale, out, (float*)workspace,
-                                             (hipStream_t)stream));
+                                             softmax_scale, out, workspace, (hipStream_t)stream));
 }
 
 const char* think_status_string(int status) {

@@ -51,6 +51,14 @@ __device__ __forceinline__ void unpack(const uint4& v, float (&x)[8], Elem<THINK
     x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
 }
 
+// 16-byte streaming load marked non-temporal: data read once per call is
+// not kept in the caches.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ldg_stream(const void* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ int clamp_len(const int32_t* seq_lens, int b, int s_cap) {
     int n = seq_lens[b];
     return n < 0 ? 0 : (n > s_cap ? s_cap : n);
@@ -72,11 +80,11 @@ struct ScoreGeom {
 ScoreGeom score_geom(const think_dims& d);
 
 struct DecodeGeom {
-    int chunk;       // tokens per workgroup
-    int nsplit;      // splits per sequence
-    int rec;         // floats per partial record: m, l, 2 pad, o[D]
-    bool mfma;       // bf16 matrix-core kernel
-    size_t ws_bytes; // [B][Hq][nsplit][rec] fp32
+    int chunk;        // tokens per workgroup
+    int nsplit;       // splits per sequence
+    int rec;          // floats per partial record: m, l, 2 pad, o[D]
+    bool mfma;        // bf16 matrix-core kernel
+    size_t ws_bytes;  // records [B][Hq][nsplit][rec] fp32
 };
 DecodeGeom decode_geom(const think_dims& d, int keep);
 
@@ -100,6 +108,6 @@ hipError_t launch_compact(const think_dims& d, const CompactGeom& g, const void*
 hipError_t launch_decode(const think_dims& d, const DecodeGeom& g, const void* q,
                          const void* k_thin, const void* v_cache, const int32_t* seq_lens,
                          const int32_t* kept_idx, int keep, float scale, void* out,
-                         float* partials, hipStream_t s);
+                         void* workspace, hipStream_t s);
 
 }  // namespace thinkkv

@@ -83,6 +83,8 @@ FAKE = ctypes.c_void_p(0x100000)      # never dereferenced: every call fails val
     (dict(D=264), -5),
     (dict(Hq=136, Hkv=8), -5),          # group of 17 query heads
     (dict(Hkv=65, Hq=65, D=256), -5),   # token row above 32 KiB
+    (dict(B=65536), -5),
+    (dict(B=16, S=1 << 28), -5),        # more than 2^31 token rows in all
 ])
 def test_score_rejects_bad_dims(L, kw, status):
     d = dims(L, **kw)

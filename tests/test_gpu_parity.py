@@ -199,3 +199,27 @@ def test_zero_length_sequence_gives_zero_scores_and_output():
     assert (to_host(s)[1] == 0).all()
     assert (to_host(out)[1] == 0).all()
     assert (to_host(thin)[1] == 0).all()
+
+
+def test_decode_workspace_reused_across_calls_and_shapes():
+    """One workspace, filled with garbage first, serves consecutive calls of
+    different shapes: no state survives between calls."""
+    qdk = _qdk()
+    cases = [(31, [4000, 2222], 4, 1, 64), (32, [700], 8, 2, 51), (33, [129, 1, 5000], 2, 2, 96)]
+    ws = torch.full((1 << 22,), 0xA5, dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        for seed, lens, Hq, Hkv, keep in cases:
+            cfg, L, q = _custom(seed, lens, batch=len(lens), n_q_heads=Hq * Hkv, n_kv_heads=Hkv,
+                                head_dim=128, seq_capacity=max(lens), keep=keep, dtype="bf16",
+                                obs_window=4, lowrank=8)
+            rng = np.random.default_rng(seed)
+            idx = np.sort(np.stack([np.stack([rng.choice(128, keep, replace=False) for _ in range(Hkv)])
+                                    for _ in range(len(lens))]), axis=-1).astype(np.int32)
+            thin = oracle.compact(L["k_cache"], L["seq_lens"], idx)
+            dims = qdk.make_dims(len(lens), Hq * Hkv, Hkv, 128, max(lens), torch.bfloat16)
+            assert qdk.think_decode_workspace_bytes(dims, keep) <= ws.numel()
+            out = qdk.think_decode_attn(to_dev(q), to_dev(thin), to_dev(L["v_cache"]),
+                                        to_dev(L["seq_lens"]), to_dev(idx), 0.1, workspace=ws)
+            torch.cuda.synchronize()
+            ref = oracle.decode(q, thin, L["v_cache"], L["seq_lens"], idx, np.float32(0.1))
+            assert row_rel_err(out, ref).max() <= 2e-2, (rep, seed)
