@@ -47,6 +47,13 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0,
                     help="approximate seconds of oracle work in the CPU baseline sample")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="run one device copy of this many MiB first (hardware-counter scaling)")
+    ap.add_argument("--no-kernel-timing", action="store_true",
+                    help="skip the per-launch event pass (hardware-counter runs)")
+    ap.add_argument("--decode-steps", type=int, default=0,
+                    help="override the workload's decode steps (profiling runs only; "
+                         "reported in config)")
     return ap.parse_args()
 
 
@@ -129,6 +136,30 @@ class Workload:
                             P(e["v"].data_ptr()), P(e["lens"].data_ptr()), P(e["idx"].data_ptr())))
             self.dec_args.append(row)
 
+    def decode_kernel_times(self, stream, torch):
+        """One step's decode calls in split-phase form, with HIP events on the
+        launch stream around every chunk-pass launch: the chunk pass's mean
+        launch duration in microseconds."""
+        from query_driven_kv_amd import _lib
+        lib, P = _lib.lib, ctypes.c_void_p
+        d, keep = ctypes.byref(self.dims), self.cfg.keep
+        out, ws, wsn = P(self.out.data_ptr()), P(self.ws_d.data_ptr()), self.ws_d.numel()
+        n = sum(len(r) for r in self.dec_args)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        k = 0
+        for row in self.dec_args:
+            for (q, thin, v, lens, idx) in row:
+                ev[k][0].record()
+                _lib.check("think_decode_attn_partial", lib.think_decode_attn_partial(
+                    d, q, thin, v, lens, idx, keep, self.scale, ws, wsn, stream))
+                ev[k][1].record()
+                _lib.check("think_decode_attn_combine", lib.think_decode_attn_combine(
+                    d, lens, keep, out, ws, wsn, stream))
+                k += 1
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3, n
+
     def decode(self, stream, steps=None):
         from query_driven_kv_amd import _lib
         lib, P = _lib.lib, ctypes.c_void_p
@@ -154,6 +185,31 @@ class Workload:
         dec_call = Kt + K + 2 * q          # |K_thin| + |V| + |q| + |out|  (|V| == |K|)
         return dict(tokens=tok, sc_layer=sc_layer, dec_call=dec_call,
                     sc_min_layer=K + Kt + Qw)
+
+
+def decode_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("decode_mfma.hip", "decode.hip", "think_common.h"):
+        with open(os.path.join(ROOT, "query_driven_kv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload):
+    """HBM bytes per chunk-pass launch from the committed hardware-counter
+    summary, if it was taken on this workload with the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "decode_mfma_llama3-8b-128k_counters.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None, "no counter summary"
+    if rec.get("workload") != workload:
+        return None, "counters taken on another workload"
+    if rec.get("source_hash") != decode_source_hash():
+        return None, "kernel changed since the counters were taken"
+    return int(rec["hbm_bytes_per_launch"]), rec.get("command", "")
 
 
 def cpu_baseline(wl, budget_s):
@@ -206,9 +262,20 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     cfg = kvsynth.CONFIGS[args.workload]
+    if args.decode_steps > 0:
+        import dataclasses
+        cfg = dataclasses.replace(cfg, decode_steps=args.decode_steps)
     log(f"workload {cfg.name}: {cfg.layers} layers, B={cfg.batch}, S={cfg.seq_capacity}, "
         f"Hq={cfg.n_q_heads}, Hkv={cfg.n_kv_heads}, D={cfg.head_dim}, keep={cfg.keep}, "
         f"{cfg.decode_steps} decode steps")
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {args.calibrate_copy_mib} MiB done")
+        del src, dst
     wl = Workload(cfg, torch, qdk, dev)
     wl.prepare_decode()
     stream = torch.cuda.current_stream()
@@ -249,6 +316,15 @@ def main():
     dec_gbs = n_dec * bm["dec_call"] / (dec_ms / 1e3) / 1e9
     dec_call_us = dec_ms * 1e3 / n_dec
     near = int(sum(int(e["tie"].sum().item()) for e in wl.layers))
+    # the dominant kernel's own launch duration, live, with HIP events (a
+    # separate pass after the timed region, so the events do not perturb it)
+    if args.no_kernel_timing:
+        part_us, n_part = float("nan"), 0
+    else:
+        part_us, n_part = wl.decode_kernel_times(sp, torch)
+        log(f"chunk-pass kernel: {part_us:.2f} us mean over {n_part} launches")
+    achieved = bm["dec_call"] / (part_us * 1e-6) / 1e9 if n_part else None
+    traffic, traffic_src = committed_traffic(cfg.name)
 
     result = {
         "metric": METRIC,
@@ -282,13 +358,16 @@ def main():
                        "kv_tokens_per_s": float(f"{tok * n_dec / (dec_ms / 1e3):.4g}"),
                        "bytes_per_call": bm["dec_call"]},
         },
-        "roofline": {"kernel": "think_decode_attn (pruned-K split-K decode)",
-                     "bound": "hbm", "achieved": round(bm["dec_call"] / (dec_call_us * 1e-6) / 1e9, 1),
+        "roofline": {"kernel": "k_decode_mfma (think_decode_attn chunk pass)",
+                     "bound": "hbm", "achieved": round(achieved, 1) if achieved else None,
                      "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": round(bm["dec_call"] / (dec_call_us * 1e-6) / 1e9 / PEAK_GBS, 4),
-                     "traffic": None,
-                     "timing": (f"HIP events on the launch stream around the {n_dec} decode "
-                                f"launches of each timed step; per-launch mean")},
+                     "frac": round(achieved / PEAK_GBS, 4) if achieved else None,
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": bm["dec_call"],
+                     "launch_us": round(part_us, 2) if n_part else None,
+                     "timing": (f"HIP events on the launch stream around each of the {n_part} "
+                                f"chunk-pass launches of one step, after the timed steps"),
+                     "traffic_source": traffic_src},
         "near_ties": near,
     }
     if not args.no_cpu_baseline:

@@ -156,6 +156,25 @@ THINK_API int think_decode_attn(const think_dims *d, const void *q, const void *
                       int32_t keep, float softmax_scale, void *out, void *workspace,
                       size_t workspace_bytes, void *stream);
 
+/*
+ * Split-phase form of think_decode_attn, same arguments and workspace.
+ * think_decode_attn_partial runs the chunk pass: every (b, kv head, token
+ * chunk) writes one partial softmax record per query head (running max,
+ * sum and unnormalised output) into the workspace.  think_decode_attn_combine
+ * merges the records of each (b, h) in ascending chunk order and writes out.
+ * Calling the two on one stream is exactly think_decode_attn (bitwise); a
+ * caller may instead run the merge on a second stream after an event so it
+ * overlaps other work.  The merge reads only dims, seq_lens, keep and the
+ * workspace the chunk pass of the same shape filled.
+ */
+THINK_API int think_decode_attn_partial(const think_dims *d, const void *q, const void *k_thin,
+                                        const void *v_cache, const int32_t *seq_lens,
+                                        const int32_t *kept_idx, int32_t keep, float softmax_scale,
+                                        void *workspace, size_t workspace_bytes, void *stream);
+THINK_API int think_decode_attn_combine(const think_dims *d, const int32_t *seq_lens, int32_t keep,
+                                        void *out, const void *workspace, size_t workspace_bytes,
+                                        void *stream);
+
 /* Static description of a status code. */
 THINK_API const char *think_status_string(int status);
 /* The hipError_t of the last THINK_ERR_HIP on this thread (0 if none). */

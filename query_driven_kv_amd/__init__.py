@@ -18,6 +18,7 @@ from . import _lib
 from ._lib import THINK_BF16, THINK_F32, ThinkError, think_dims
 
 __all__ = ["think_score", "think_select", "think_compact_k", "think_decode_attn",
+           "think_decode_attn_partial", "think_decode_attn_combine",
            "think_keep_from_ratio", "think_score_workspace_bytes", "think_decode_workspace_bytes",
            "think_abi_version", "make_dims", "ThinkError", "think_dims", "LIB_PATH"]
 
@@ -158,4 +159,38 @@ def think_decode_attn(q, k_thin, v_cache, seq_lens, kept_idx, softmax_scale, *, 
         ctypes.byref(dims), _p(q), _p(k_thin), _p(v_cache), _p(seq_lens), _p(kept_idx), int(keep),
         float(softmax_scale), _p(out), _p(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+    return out
+
+
+def _decode_dims(q, k_thin, v_cache, seq_lens, kept_idx):
+    _dev(q, k_thin, v_cache, seq_lens, kept_idx)
+    _i32(seq_lens, "seq_lens")
+    _i32(kept_idx, "kept_idx")
+    B, Hq, D = q.shape
+    _, S, Hkv, keep = k_thin.shape
+    if (tuple(v_cache.shape) != (B, S, Hkv, D) or tuple(kept_idx.shape) != (B, Hkv, keep)
+            or k_thin.dtype != q.dtype or v_cache.dtype != q.dtype):
+        raise ValueError("shape or dtype mismatch between q, k_thin, v_cache and kept_idx")
+    return make_dims(B, Hq, Hkv, D, S, _dtype_code(q)), keep
+
+
+def think_decode_attn_partial(q, k_thin, v_cache, seq_lens, kept_idx, softmax_scale, workspace,
+                              *, stream=None):
+    """Chunk pass of stage (d): per-chunk partial softmax records into `workspace`
+    (uint8, >= think_decode_workspace_bytes).  Returns (dims, keep) for the merge."""
+    dims, keep = _decode_dims(q, k_thin, v_cache, seq_lens, kept_idx)
+    _dev(workspace)
+    _lib.check("think_decode_attn_partial", _lib.lib.think_decode_attn_partial(
+        ctypes.byref(dims), _p(q), _p(k_thin), _p(v_cache), _p(seq_lens), _p(kept_idx), int(keep),
+        float(softmax_scale), _p(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return dims, keep
+
+
+def think_decode_attn_combine(dims, keep, seq_lens, workspace, out, *, stream=None):
+    """Merge pass of stage (d): merges the records the chunk pass left in `workspace`."""
+    _dev(seq_lens, workspace, out)
+    _lib.check("think_decode_attn_combine", _lib.lib.think_decode_attn_combine(
+        ctypes.byref(dims), _p(seq_lens), int(keep), _p(out), _p(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
     return out

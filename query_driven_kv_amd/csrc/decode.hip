@@ -201,40 +201,41 @@ DecodeGeom decode_geom(const think_dims& d, int keep) {
     return g;
 }
 
-hipError_t launch_decode(const think_dims& d, const DecodeGeom& g, const void* q,
-                         const void* k_thin, const void* v_cache, const int32_t* seq_lens,
-                         const int32_t* kept_idx, int keep, float scale, void* out,
-                         void* workspace, hipStream_t s) {
-    float* partials = reinterpret_cast<float*>(workspace);
+hipError_t launch_decode_partial(const think_dims& d, const DecodeGeom& g, const void* q,
+                                 const void* k_thin, const void* v_cache, const int32_t* seq_lens,
+                                 const int32_t* kept_idx, int keep, float scale, float* partials,
+                                 hipStream_t s) {
+    if (g.mfma)
+        return launch_decode_mfma(d, g, q, k_thin, v_cache, seq_lens, kept_idx, keep, scale,
+                                  partials, s);
     const int G = d.n_q_heads / d.n_kv_heads;
     dim3 grid(g.nsplit, d.n_kv_heads, d.batch);
-    dim3 cgrid(d.n_q_heads, d.batch);
-    int sg_count = 1024 / d.head_dim;
-    if (sg_count > 16) sg_count = 16;
-    const int cthreads = d.head_dim * sg_count;
-    if (g.mfma) {
-        hipError_t e = launch_decode_mfma(d, g, q, k_thin, v_cache, seq_lens, kept_idx, keep,
-                                          scale, partials, s);
-        if (e != hipSuccess) return e;
-        k_decode_combine<THINK_BF16><<<cgrid, cthreads, 0, s>>>(
-            partials, seq_lens, d.seq_capacity, g.chunk, g.nsplit, g.rec, d.head_dim, sg_count,
-            (uint16_t*)out);
-    } else if (d.dtype == THINK_BF16) {
+    if (d.dtype == THINK_BF16)
         k_decode_partial<THINK_BF16><<<grid, kThreads, 0, s>>>(
             (const uint16_t*)q, (const uint16_t*)k_thin, (const uint16_t*)v_cache, seq_lens,
             kept_idx, d.seq_capacity, d.n_kv_heads, G, d.head_dim, keep, scale, g.nsplit, g.rec,
             partials);
-        k_decode_combine<THINK_BF16><<<cgrid, cthreads, 0, s>>>(
-            partials, seq_lens, d.seq_capacity, g.chunk, g.nsplit, g.rec, d.head_dim, sg_count,
-            (uint16_t*)out);
-    } else {
+    else
         k_decode_partial<THINK_F32><<<grid, kThreads, 0, s>>>(
             (const float*)q, (const float*)k_thin, (const float*)v_cache, seq_lens, kept_idx,
             d.seq_capacity, d.n_kv_heads, G, d.head_dim, keep, scale, g.nsplit, g.rec, partials);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_combine(const think_dims& d, const DecodeGeom& g, const int32_t* seq_lens,
+                                 void* out, const float* partials, hipStream_t s) {
+    dim3 cgrid(d.n_q_heads, d.batch);
+    int sg_count = 1024 / d.head_dim;
+    if (sg_count > 16) sg_count = 16;
+    const int cthreads = d.head_dim * sg_count;
+    if (d.dtype == THINK_BF16)
+        k_decode_combine<THINK_BF16><<<cgrid, cthreads, 0, s>>>(
+            partials, seq_lens, d.seq_capacity, g.chunk, g.nsplit, g.rec, d.head_dim, sg_count,
+            (uint16_t*)out);
+    else
         k_decode_combine<THINK_F32><<<cgrid, cthreads, 0, s>>>(
             partials, seq_lens, d.seq_capacity, g.chunk, g.nsplit, g.rec, d.head_dim, sg_count,
             (float*)out);
-    }
     return hipGetLastError();
 }
 

@@ -98,20 +98,68 @@ int think_compact_k(const think_dims* d, const void* k_cache, const int32_t* seq
                                               (hipStream_t)stream));
 }
 
+namespace {
+
+// Validation shared by the decode entry points, in the documented order:
+// dims, required pointers, keep, alignment, workspace.
+int check_decode(const think_dims* d, const void* q, const void* k_thin, const void* v_cache,
+                 const int32_t* seq_lens, const int32_t* kept_idx, bool need_inputs,
+                 const void* out, bool need_out, int32_t keep, const void* workspace,
+                 size_t workspace_bytes, thinkkv::DecodeGeom* g) {
+    int st = check_dims(d);
+    if (st != THINK_OK) return st;
+    if (!seq_lens) return THINK_ERR_NULL;
+    if (need_inputs && (!q || !k_thin || !v_cache || !kept_idx)) return THINK_ERR_NULL;
+    if (need_out && !out) return THINK_ERR_NULL;
+    if (keep < 1 || keep > d->head_dim) return THINK_ERR_KEEP;
+    if (need_inputs && (!aligned16(k_thin) || !aligned16(v_cache) || !aligned16(q)))
+        return THINK_ERR_UNSUPPORTED;
+    *g = thinkkv::decode_geom(*d, keep);
+    if (!workspace || workspace_bytes < g->ws_bytes || !aligned16(workspace))
+        return THINK_ERR_WORKSPACE;
+    return THINK_OK;
+}
+
+}  // namespace
+
 int think_decode_attn(const think_dims* d, const void* q, const void* k_thin,
                       const void* v_cache, const int32_t* seq_lens, const int32_t* kept_idx,
                       int32_t keep, float softmax_scale, void* out, void* workspace,
                       size_t workspace_bytes, void* stream) {
-    int st = check_dims(d);
+    thinkkv::DecodeGeom g;
+    int st = check_decode(d, q, k_thin, v_cache, seq_lens, kept_idx, true, out, true, keep,
+                          workspace, workspace_bytes, &g);
     if (st != THINK_OK) return st;
-    if (!q || !k_thin || !v_cache || !seq_lens || !kept_idx || !out) return THINK_ERR_NULL;
-    if (keep < 1 || keep > d->head_dim) return THINK_ERR_KEEP;
-    if (!aligned16(k_thin) || !aligned16(v_cache) || !aligned16(q)) return THINK_ERR_UNSUPPORTED;
-    const thinkkv::DecodeGeom g = thinkkv::decode_geom(*d, keep);
-    if (!workspace || workspace_bytes < g.ws_bytes || !aligned16(workspace))
-        return THINK_ERR_WORKSPACE;
-    return hip_status(thinkkv::launch_decode(*d, g, q, k_thin, v_cache, seq_lens, kept_idx, keep,
-                                             softmax_scale, out, workspace, (hipStream_t)stream));
+    st = hip_status(thinkkv::launch_decode_partial(*d, g, q, k_thin, v_cache, seq_lens, kept_idx,
+                                                   keep, softmax_scale, (float*)workspace,
+                                                   (hipStream_t)stream));
+    if (st != THINK_OK) return st;
+    return hip_status(thinkkv::launch_decode_combine(*d, g, seq_lens, out, (const float*)workspace,
+                                                     (hipStream_t)stream));
+}
+
+int think_decode_attn_partial(const think_dims* d, const void* q, const void* k_thin,
+                              const void* v_cache, const int32_t* seq_lens,
+                              const int32_t* kept_idx, int32_t keep, float softmax_scale,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    thinkkv::DecodeGeom g;
+    int st = check_decode(d, q, k_thin, v_cache, seq_lens, kept_idx, true, nullptr, false, keep,
+                          workspace, workspace_bytes, &g);
+    if (st != THINK_OK) return st;
+    return hip_status(thinkkv::launch_decode_partial(*d, g, q, k_thin, v_cache, seq_lens, kept_idx,
+                                                     keep, softmax_scale, (float*)workspace,
+                                                     (hipStream_t)stream));
+}
+
+int think_decode_attn_combine(const think_dims* d, const int32_t* seq_lens, int32_t keep,
+                              void* out, const void* workspace, size_t workspace_bytes,
+                              void* stream) {
+    thinkkv::DecodeGeom g;
+    int st = check_decode(d, nullptr, nullptr, nullptr, seq_lens, nullptr, false, out, true, keep,
+                          workspace, workspace_bytes, &g);
+    if (st != THINK_OK) return st;
+    return hip_status(thinkkv::launch_decode_combine(*d, g, seq_lens, out, (const float*)workspace,
+                                                     (hipStream_t)stream));
 }
 
 const char* think_status_string(int status) {

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_header_declarations_are_all_exported(L):
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 12
     assert sorted(L.EXPORTS) == names
     so = ctypes.CDLL(L.LIB_PATH)
     for n in names:
@@ -120,6 +120,16 @@ def test_null_keep_window_workspace_and_alignment(L):
                                  FAKE, 64, None) == -6
     assert lib.think_decode_attn(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, 8, 0.1, FAKE,
                                  FAKE, big, None) == -1
+    assert lib.think_decode_attn_partial(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0.1,
+                                         FAKE, big, None) == -3
+    assert lib.think_decode_attn_partial(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, 8, 0.1,
+                                         FAKE, big, None) == -1
+    assert lib.think_decode_attn_partial(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 8, 0.1,
+                                         FAKE, 16, None) == -6
+    assert lib.think_decode_attn_combine(ctypes.byref(d), FAKE, 8, None, FAKE, big, None) == -1
+    assert lib.think_decode_attn_combine(ctypes.byref(d), FAKE, 8, FAKE, FAKE, 16, None) == -6
+    assert lib.think_decode_attn_combine(ctypes.byref(dims(L, Hq=30)), FAKE, 8, FAKE, FAKE, big,
+                                         None) == -2
 
 
 def test_status_strings(L):

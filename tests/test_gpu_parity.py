@@ -223,3 +223,25 @@ def test_decode_workspace_reused_across_calls_and_shapes():
             torch.cuda.synchronize()
             ref = oracle.decode(q, thin, L["v_cache"], L["seq_lens"], idx, np.float32(0.1))
             assert row_rel_err(out, ref).max() <= 2e-2, (rep, seed)
+
+
+def test_split_phase_decode_is_bitwise_the_single_call():
+    qdk = _qdk()
+    for seed, lens, Hq, Hkv, D, keep, dtype in [(40, [3000, 17], 8, 2, 128, 64, "bf16"),
+                                                (41, [900], 6, 3, 64, 20, "f32"),
+                                                (42, [2048, 2047], 32, 8, 128, 77, "bf16")]:
+        cfg, L, q = _custom(seed, lens, batch=len(lens), n_q_heads=Hq, n_kv_heads=Hkv,
+                            head_dim=D, seq_capacity=max(lens), keep=keep, dtype=dtype,
+                            obs_window=4)
+        k, v, lensd, qd = to_dev(L["k_cache"]), to_dev(L["v_cache"]), to_dev(L["seq_lens"]), to_dev(q)
+        s = qdk.think_score(k, lensd, to_dev(L["q_obs"]))
+        idx, _ = qdk.think_select(s, keep)
+        thin = qdk.think_compact_k(k, lensd, idx)
+        one = qdk.think_decode_attn(qd, thin, v, lensd, idx, 0.125)
+        dims = qdk.make_dims(len(lens), Hq, Hkv, D, max(lens), qd.dtype)
+        ws = torch.empty(qdk.think_decode_workspace_bytes(dims, keep), dtype=torch.uint8, device="cuda")
+        dims, kk = qdk.think_decode_attn_partial(qd, thin, v, lensd, idx, 0.125, ws)
+        two = qdk.think_decode_attn_combine(dims, kk, lensd, ws, torch.empty_like(one))
+        torch.cuda.synchronize()
+        assert torch.equal(one.view(torch.int16) if one.dtype == torch.bfloat16 else one.view(torch.int32),
+                           two.view(torch.int16) if two.dtype == torch.bfloat16 else two.view(torch.int32))
