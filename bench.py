@@ -2,7 +2,7 @@
 """Throughput of the key-channel pruning hot path on one MI355X.
 
 One step = the whole path over one batch of synthetic input:
-  for every layer: think_score -> think_select -> think_compact_k
+  for every layer: think_score_select (scores + kept channels) -> think_compact_k
   then for every decode step and every layer: think_decode_attn
 Default workload: the 32-layer LLaMA-3-8B-like cache, 131072 tokens per
 layer, 32 q / 8 kv heads, head_dim 128, window 64, keep 64 of 128 (bf16),
@@ -110,16 +110,14 @@ class Workload:
     def score_compact(self, stream):
         from query_driven_kv_amd import _lib
         lib, P = _lib.lib, ctypes.c_void_p
-        d, sd, keep = ctypes.byref(self.dims), ctypes.byref(self.sel_dims), self.cfg.keep
+        d, keep = ctypes.byref(self.dims), self.cfg.keep
         W = self.cfg.obs_window
         ws, wsn = P(self.ws_s.data_ptr()), self.ws_s.numel()
         for e in self.layers:
-            _lib.check("think_score", lib.think_score(
-                d, P(e["k"].data_ptr()), P(e["lens"].data_ptr()), P(e["qo"].data_ptr()), W,
-                P(e["scores"].data_ptr()), ws, wsn, stream))
-            _lib.check("think_select", lib.think_select(
-                sd, P(e["scores"].data_ptr()), keep, P(e["idx"].data_ptr()),
-                P(e["tie"].data_ptr()), stream))
+            _lib.check("think_score_select", lib.think_score_select(
+                d, P(e["k"].data_ptr()), P(e["lens"].data_ptr()), P(e["qo"].data_ptr()), W, keep,
+                P(e["scores"].data_ptr()), P(e["idx"].data_ptr()), P(e["tie"].data_ptr()), ws, wsn,
+                stream))
             _lib.check("think_compact_k", lib.think_compact_k(
                 d, P(e["k"].data_ptr()), P(e["lens"].data_ptr()), P(e["idx"].data_ptr()), keep,
                 P(e["thin"].data_ptr()), stream))

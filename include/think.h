@@ -123,6 +123,18 @@ THINK_API int think_select(const think_dims *d, const float *scores, int32_t kee
                            int32_t *near_tie, void *stream);
 
 /*
+ * Stages (a) and (b) fused: the scores of think_score and the selection of
+ * think_select in two launches instead of three (the selection runs in the
+ * workgroup that finishes each (b, kv) row's scores).  Results are bitwise
+ * those of think_score followed by think_select.  scores may be NULL (not
+ * written); near_tie may be NULL.  Workspace as for think_score.
+ */
+THINK_API int think_score_select(const think_dims *d, const void *k_cache, const int32_t *seq_lens,
+                                 const void *q_obs, int32_t obs_window, int32_t keep,
+                                 float *scores, int32_t *kept_idx, int32_t *near_tie,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Stage (c) - the thinner key cache ("ThinK", title and Technical framework:
  * inference proceeds on the pruned key cache).  A byte copy:
  *   k_thin[b,t,kv,j] = k_cache[b,t,kv,kept_idx[b,kv,j]]   for t < len_b

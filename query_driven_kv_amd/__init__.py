@@ -17,7 +17,8 @@ import torch
 from . import _lib
 from ._lib import THINK_BF16, THINK_F32, ThinkError, think_dims
 
-__all__ = ["think_score", "think_select", "think_compact_k", "think_decode_attn",
+__all__ = ["think_score", "think_score_select", "think_select", "think_compact_k",
+           "think_decode_attn",
            "think_decode_attn_partial", "think_decode_attn_combine",
            "think_keep_from_ratio", "think_score_workspace_bytes", "think_decode_workspace_bytes",
            "think_abi_version", "make_dims", "ThinkError", "think_dims", "LIB_PATH"]
@@ -98,6 +99,34 @@ def think_score(k_cache, seq_lens, q_obs, *, scores=None, workspace=None, stream
         ctypes.byref(dims), _p(k_cache), _p(seq_lens), _p(q_obs), W, _p(scores), _p(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return scores
+
+
+def think_score_select(k_cache, seq_lens, q_obs, keep, *, scores=None, kept_idx=None,
+                       near_tie=None, workspace=None, stream=None):
+    """Stages (a)+(b) fused.  Returns (scores fp32 [B,Hkv,D], kept_idx int32
+    [B,Hkv,keep], near_tie int32 [B,Hkv]); bitwise think_score then think_select."""
+    _dev(k_cache, seq_lens, q_obs, scores, kept_idx, near_tie, workspace)
+    _i32(seq_lens, "seq_lens")
+    B, S, Hkv, D = k_cache.shape
+    Bq, W, Hq, Dq = q_obs.shape
+    if (Bq, Dq) != (B, D) or q_obs.dtype != k_cache.dtype or tuple(seq_lens.shape) != (B,):
+        raise ValueError("shape or dtype mismatch between k_cache, q_obs and seq_lens")
+    dims = make_dims(B, Hq, Hkv, D, S, _dtype_code(k_cache))
+    dev = k_cache.device
+    if scores is None:
+        scores = torch.empty(B, Hkv, D, dtype=torch.float32, device=dev)
+    if kept_idx is None:
+        kept_idx = torch.empty(B, Hkv, max(int(keep), 0), dtype=torch.int32, device=dev)
+    if near_tie is None:
+        near_tie = torch.empty(B, Hkv, dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(think_score_workspace_bytes(dims), 16), dtype=torch.uint8,
+                                device=dev)
+    _lib.check("think_score_select", _lib.lib.think_score_select(
+        ctypes.byref(dims), _p(k_cache), _p(seq_lens), _p(q_obs), W, int(keep), _p(scores),
+        _p(kept_idx), _p(near_tie), _p(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return scores, kept_idx, near_tie
 
 
 def think_select(scores, keep, *, kept_idx=None, near_tie=None, want_near_tie=True, stream=None):

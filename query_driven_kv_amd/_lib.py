@@ -16,7 +16,8 @@ STATUS = {0: "THINK_OK", -1: "THINK_ERR_NULL", -2: "THINK_ERR_SHAPE", -3: "THINK
 
 # every function include/think.h declares
 EXPORTS = ("think_abi_version", "think_keep_from_ratio", "think_score_workspace_bytes",
-           "think_decode_workspace_bytes", "think_score", "think_select", "think_compact_k",
+           "think_decode_workspace_bytes", "think_score", "think_score_select", "think_select",
+           "think_compact_k",
            "think_decode_attn", "think_decode_attn_partial", "think_decode_attn_combine",
            "think_status_string", "think_last_hip_error")
 
@@ -58,6 +59,7 @@ def _load():
     l.think_decode_workspace_bytes.argtypes = [pd, i32]
     l.think_decode_workspace_bytes.restype = sz
     l.think_score.argtypes = [pd, vp, vp, vp, i32, vp, vp, sz, vp]
+    l.think_score_select.argtypes = [pd, vp, vp, vp, i32, i32, vp, vp, vp, vp, sz, vp]
     l.think_select.argtypes = [pd, vp, i32, vp, vp, vp]
     l.think_compact_k.argtypes = [pd, vp, vp, vp, i32, vp, vp]
     l.think_decode_attn.argtypes = [pd, vp, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp, sz, vp]
@@ -66,7 +68,8 @@ def _load():
     l.think_status_string.argtypes = [ctypes.c_int]
     l.think_status_string.restype = ctypes.c_char_p
     l.think_last_hip_error.restype = ctypes.c_int
-    for name in ("think_score", "think_select", "think_compact_k", "think_decode_attn",
+    for name in ("think_score", "think_score_select", "think_select", "think_compact_k",
+                 "think_decode_attn",
                  "think_decode_attn_partial", "think_decode_attn_combine"):
         getattr(l, name).restype = ctypes.c_int
     return l

@@ -12,7 +12,8 @@
 // gathered from LDS through a per-workgroup source map.  This keeps stores
 // 16-byte wide even when keep is odd (per-head thin rows of 154 or 102 bytes).
 // Only the two 16-byte chunks at the ends of the range can be partial; those
-// are written element by element.  A pure copy: bit-exact by construction.
+// are written element by element.  Loads and stores are non-temporal (each
+// byte is touched once per call).  A pure copy: bit-exact by construction.
 #include "think_common.h"
 
 namespace thinkkv {
@@ -45,7 +46,7 @@ __global__ __launch_bounds__(kThreads) void k_compact(
     }
     const int nvec = nt * R * (int)sizeof(E) / 16;
     const uint4* src = reinterpret_cast<const uint4*>(k_cache + ((size_t)b * s_cap + t0) * R);
-    for (int v = tid; v < nvec; v += kThreads) lds[v] = src[v];
+    for (int v = tid; v < nvec; v += kThreads) lds[v] = ldg_stream(src + v);
     __syncthreads();
 
     const size_t E0 = ((size_t)b * s_cap + t0) * Ro;
@@ -62,7 +63,8 @@ __global__ __launch_bounds__(kThreads) void k_compact(
                 pack.e[k] = rows[r * R + srcmap[o]];
                 if (++o == Ro) { o = 0; ++r; }
             }
-            *reinterpret_cast<uint4*>(k_thin + lo) = pack.v;
+            __builtin_nontemporal_store(u32x4_t{pack.v.x, pack.v.y, pack.v.z, pack.v.w},
+                                        reinterpret_cast<u32x4_t*>(k_thin + lo));
         } else {
             const size_t a = lo > E0 ? lo : E0;
             const size_t z = lo + CE < E1 ? lo + CE : E1;
@@ -80,7 +82,9 @@ __global__ __launch_bounds__(kThreads) void k_compact(
 CompactGeom compact_geom(const think_dims& d, int keep) {
     CompactGeom g{};
     const int row_bytes = d.n_kv_heads * d.head_dim * elem_bytes(d.dtype);
-    int tile = 32768 / row_bytes;
+    // 16 KiB tiles (8 rows of a 2 KiB row): enough workgroups per CU to keep
+    // the loads and stores of several tiles in flight
+    int tile = 16384 / row_bytes;
     if (tile > 64) tile = 64;
     if (tile < 1) tile = 1;
     g.tile = tile;

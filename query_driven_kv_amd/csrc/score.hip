@@ -16,14 +16,16 @@
 //                     in a fixed order and written as one fp32 partial per
 //                     (split, channel).
 //   k_score_finalize  one workgroup per (b, kv): sums the splits in fp64 in a
-//                     fixed order, forms the window-query norms and the score.
+//                     fixed order, forms the score and optionally selects the
+//                     kept channels right there.
 // No atomics: results are bitwise reproducible.
-#include "think_common.h"
+#include "select_row.h"
 
 namespace thinkkv {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;   // partial pass: ~256 workgroups of 8 waves stream K best
+constexpr int kColGroup = 256;  // 16-byte column vectors per workgroup
 constexpr int kRun = 16;   // tokens per fp32 run before folding into fp64
 
 template <int DT>
@@ -38,8 +40,8 @@ __global__ __launch_bounds__(kThreads) void k_score_partial(
     if (t0 >= len) return;                       // finalize never reads this split
     const int t1 = min(t0 + tpw, len);
 
-    const int v0 = cg * kThreads;
-    const int nvg = min(kThreads, nvec - v0);    // vectors in this column group
+    const int v0 = cg * kColGroup;
+    const int nvg = min(kColGroup, nvec - v0);    // vectors in this column group
     const int rpi = kThreads / nvg;              // token rows covered per step
     const int tid = threadIdx.x;
     const bool active = tid < rpi * nvg;
@@ -89,53 +91,120 @@ __global__ __launch_bounds__(kThreads) void k_score_partial(
     }
 }
 
-template <int DT>
+// One workgroup per (b, kv), blockDim = (D/4) x SG threads.
+//  K2:  thread (channel quad cq, split group sg) sums splits sg, sg+SG, ...
+//       in ascending order, reading float4 partials eight splits at a time
+//       so the loads overlap; the SG group sums are added in ascending order.
+//  Q:   the group's window rows hold G*D contiguous query elements; thread
+//       (16-byte vector v, row group rg) sums the squares of its vector over
+//       a contiguous range of rows (loads issued eight rows at a time); the
+//       row groups are added in ascending order.
+//  s  = sqrt(K2) * sum_g sqrt(Q2[g]), fp64, stored as fp32; with SELECT the
+//       same workgroup then picks the kept channels (select_row.h).
+template <int DT, bool SELECT>
 __global__ __launch_bounds__(1024) void k_score_finalize(
         const float* __restrict__ partials, const int32_t* __restrict__ seq_lens, int s_cap,
         int tpw, int nsplit, const typename Elem<DT>::T* __restrict__ q_obs, int W, int Hq,
-        int Hkv, int D, int sg_count, float* __restrict__ scores) {
+        int Hkv, int D, float* __restrict__ scores, int keep, int32_t* __restrict__ kept_idx,
+        int32_t* __restrict__ near_tie) {
     using E = Elem<DT>;
+    constexpr int EPV = E::kPerVec;
     const int kv = blockIdx.x, b = blockIdx.y;
-    const int tid = threadIdx.x;
-    const int c = tid % D, sg = tid / D;
-    const int G = Hq / Hkv;
+    const int tid = threadIdx.x, nth = blockDim.x;
+    const int G = Hq / Hkv, R = Hkv * D, Q = D / 4, SG = nth / Q;
     const int len = clamp_len(seq_lens, b, s_cap);
     const int ns = (len + tpw - 1) / tpw;
-    const int R = Hkv * D;
 
-    // Sub-group sg sums splits sg, sg+SG, sg+2SG, ... into four interleaved
-    // fp64 accumulators (independent loads), combined in a fixed order.
-    const float* p = partials + (size_t)b * nsplit * R + (size_t)kv * D + c;
-    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
-    int s = sg;
-    for (; s + 3 * sg_count < ns; s += 4 * sg_count) {
-        a0 += (double)p[(size_t)s * R];
-        a1 += (double)p[(size_t)(s + sg_count) * R];
-        a2 += (double)p[(size_t)(s + 2 * sg_count) * R];
-        a3 += (double)p[(size_t)(s + 3 * sg_count) * R];
-    }
-    for (; s < ns; s += sg_count) a0 += (double)p[(size_t)s * R];
-    const double k2 = (a0 + a1) + (a2 + a3);
+    __shared__ double red[4096];                 // [SG][D] split-group sums, then [RG][G*D]
+    __shared__ double qn[4096];                  // [g][c] sqrt(Q2)  (G * D <= 4096)
+    __shared__ float s_sc[256];
+    __shared__ int s_scratch[1024];
+    __shared__ float s_cut[2];
 
-    __shared__ double kred[1024];
-    __shared__ double qn[16 * 256];
-    kred[tid] = k2;
-    for (int g = sg; g < G; g += sg_count) {
-        const int h = kv * G + g;
-        double q2 = 0.0;
-        for (int i = 0; i < W; ++i) {
-            const double x = E::load(q_obs, (((size_t)b * W + i) * Hq + h) * D + c);
-            q2 += x * x;
+    {
+        const int cq = tid % Q, sg = tid / Q;
+        const float4* p = reinterpret_cast<const float4*>(partials + (size_t)b * nsplit * R +
+                                                          (size_t)kv * D) + cq;
+        const size_t sstride = (size_t)R / 4;
+        double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+        for (int s0 = sg; s0 < ns; s0 += 8 * SG) {
+            float4 v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int sp = s0 + k * SG;
+                v[k] = sp < ns ? p[(size_t)sp * sstride] : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                a0 += (double)v[k].x;
+                a1 += (double)v[k].y;
+                a2 += (double)v[k].z;
+                a3 += (double)v[k].w;
+            }
         }
-        qn[g * D + c] = sqrt(q2);
+        red[sg * D + 4 * cq + 0] = a0;
+        red[sg * D + 4 * cq + 1] = a1;
+        red[sg * D + 4 * cq + 2] = a2;
+        red[sg * D + 4 * cq + 3] = a3;
     }
     __syncthreads();
-    if (sg == 0) {
-        double K2 = 0.0;
-        for (int r = 0; r < sg_count; ++r) K2 += kred[r * D + c];
+    double K2 = 0.0;
+    if (tid < D)
+        for (int r = 0; r < SG; ++r) K2 += red[r * D + tid];
+    __syncthreads();                             // red is reused below
+
+    {
+        const int GD = G * D, nv = GD / EPV;     // 16-byte vectors per window row
+        int RG = nth / nv;
+        if (RG > 4096 / GD) RG = 4096 / GD;
+        if (RG > W) RG = W;
+        if (RG < 1) RG = 1;
+        const int v = tid % nv, rg = tid / nv;
+        if (rg < RG) {
+            const uint4* qb = reinterpret_cast<const uint4*>(
+                q_obs + ((size_t)b * W * Hq + (size_t)kv * G) * D) + v;
+            const size_t rstride = (size_t)Hq * D / EPV;   // vectors between window rows
+            const int i0 = rg * W / RG, i1 = (rg + 1) * W / RG;
+            double acc[EPV];
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) acc[e] = 0.0;
+            for (int i = i0; i < i1; i += 8) {
+                uint4 x[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    x[k] = i + k < i1 ? qb[(size_t)(i + k) * rstride] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    float f[EPV];
+                    unpack(x[k], f, E{});
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) acc[e] += (double)f[e] * (double)f[e];
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) red[rg * GD + v * EPV + e] = acc[e];
+        }
+        __syncthreads();
+        for (int pr = tid; pr < GD; pr += nth) {
+            double t = 0.0;
+            for (int r = 0; r < RG; ++r) t += red[r * GD + pr];
+            qn[pr] = sqrt(t);                    // index g*D + c
+        }
+        __syncthreads();
+    }
+
+    if (tid < D) {
         double qsum = 0.0;
-        for (int g = 0; g < G; ++g) qsum += qn[g * D + c];
-        scores[((size_t)b * Hkv + kv) * D + c] = (float)(sqrt(K2) * qsum);
+        for (int g = 0; g < G; ++g) qsum += qn[g * D + tid];
+        const float sc = (float)(sqrt(K2) * qsum);
+        if (scores) scores[((size_t)b * Hkv + kv) * D + tid] = sc;
+        s_sc[tid] = sc;
+    }
+    if (SELECT) {
+        __syncthreads();
+        const size_t row = (size_t)b * Hkv + kv;
+        select_row(s_sc, D, keep, s_scratch, s_cut, kept_idx + row * keep,
+                   near_tie ? near_tie + row : nullptr);
     }
 }
 
@@ -145,10 +214,10 @@ ScoreGeom score_geom(const think_dims& d) {
     ScoreGeom g{};
     const int e = elem_bytes(d.dtype);
     g.nvec = d.n_kv_heads * d.head_dim * e / 16;
-    g.ncg = (g.nvec + kThreads - 1) / kThreads;
-    // aim for ~512 workgroups (two per CU); tokens per workgroup a multiple of 16
+    g.ncg = (g.nvec + kColGroup - 1) / kColGroup;
+    // aim for ~256 workgroups (one per CU); tokens per workgroup a multiple of 16
     const int64_t rows = (int64_t)d.seq_capacity * d.batch * g.ncg;
-    int64_t tpw = (rows + 511) / 512;
+    int64_t tpw = (rows + 255) / 256;
     tpw = (tpw + 15) / 16 * 16;
     if (tpw < 16) tpw = 16;
     if (tpw > 4096) tpw = 4096;
@@ -160,24 +229,31 @@ ScoreGeom score_geom(const think_dims& d) {
 
 hipError_t launch_score(const think_dims& d, const ScoreGeom& g, const void* k_cache,
                         const int32_t* seq_lens, const void* q_obs, int W, float* scores,
-                        float* partials, hipStream_t s) {
+                        void* workspace, int keep, int32_t* kept_idx, int32_t* near_tie,
+                        hipStream_t s) {
+    float* partials = reinterpret_cast<float*>(workspace);
     dim3 grid1(g.nsplit, g.ncg, d.batch);
-    int sg_count = 1024 / d.head_dim;
-    if (sg_count > 8) sg_count = 8;
+    const int Q = d.head_dim / 4;
+    int sg = 1024 / Q;
+    if (sg > 64) sg = 64;
     dim3 grid2(d.n_kv_heads, d.batch);
+    const int threads2 = Q * sg;
+#define THINK_FINALIZE(DT, SEL, T)                                                               \
+    k_score_finalize<DT, SEL><<<grid2, threads2, 0, s>>>(                                       \
+        partials, seq_lens, d.seq_capacity, g.tpw, g.nsplit, (const T*)q_obs, W, d.n_q_heads,   \
+        d.n_kv_heads, d.head_dim, scores, keep, kept_idx, near_tie)
     if (d.dtype == THINK_BF16) {
         k_score_partial<THINK_BF16><<<grid1, kThreads, 0, s>>>(
             (const uint4*)k_cache, seq_lens, d.seq_capacity, g.nvec, g.tpw, g.nsplit, partials);
-        k_score_finalize<THINK_BF16><<<grid2, d.head_dim * sg_count, 0, s>>>(
-            partials, seq_lens, d.seq_capacity, g.tpw, g.nsplit, (const uint16_t*)q_obs, W,
-            d.n_q_heads, d.n_kv_heads, d.head_dim, sg_count, scores);
+        if (kept_idx) THINK_FINALIZE(THINK_BF16, true, uint16_t);
+        else THINK_FINALIZE(THINK_BF16, false, uint16_t);
     } else {
         k_score_partial<THINK_F32><<<grid1, kThreads, 0, s>>>(
             (const uint4*)k_cache, seq_lens, d.seq_capacity, g.nvec, g.tpw, g.nsplit, partials);
-        k_score_finalize<THINK_F32><<<grid2, d.head_dim * sg_count, 0, s>>>(
-            partials, seq_lens, d.seq_capacity, g.tpw, g.nsplit, (const float*)q_obs, W,
-            d.n_q_heads, d.n_kv_heads, d.head_dim, sg_count, scores);
+        if (kept_idx) THINK_FINALIZE(THINK_F32, true, float);
+        else THINK_FINALIZE(THINK_F32, false, float);
     }
+#undef THINK_FINALIZE
     return hipGetLastError();
 }
 

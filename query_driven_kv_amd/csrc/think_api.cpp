@@ -71,7 +71,26 @@ int think_score(const think_dims* d, const void* k_cache, const int32_t* seq_len
     if (!workspace || workspace_bytes < g.ws_bytes || !aligned16(workspace))
         return THINK_ERR_WORKSPACE;
     return hip_status(thinkkv::launch_score(*d, g, k_cache, seq_lens, q_obs, obs_window, scores,
-                                            (float*)workspace, (hipStream_t)stream));
+                                            workspace, 0, nullptr, nullptr,
+                                            (hipStream_t)stream));
+}
+
+int think_score_select(const think_dims* d, const void* k_cache, const int32_t* seq_lens,
+                       const void* q_obs, int32_t obs_window, int32_t keep, float* scores,
+                       int32_t* kept_idx, int32_t* near_tie, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    int st = check_dims(d);
+    if (st != THINK_OK) return st;
+    if (!k_cache || !seq_lens || !q_obs || !kept_idx) return THINK_ERR_NULL;
+    if (obs_window < 1) return THINK_ERR_SHAPE;
+    if (keep < 1 || keep > d->head_dim) return THINK_ERR_KEEP;
+    if (!aligned16(k_cache)) return THINK_ERR_UNSUPPORTED;
+    const thinkkv::ScoreGeom g = thinkkv::score_geom(*d);
+    if (!workspace || workspace_bytes < g.ws_bytes || !aligned16(workspace))
+        return THINK_ERR_WORKSPACE;
+    return hip_status(thinkkv::launch_score(*d, g, k_cache, seq_lens, q_obs, obs_window, scores,
+                                            workspace, keep, kept_idx, near_tie,
+                                            (hipStream_t)stream));
 }
 
 int think_select(const think_dims* d, const float* scores, int32_t keep, int32_t* kept_idx,

@@ -71,11 +71,11 @@ inline int elem_bytes(int dtype) { return dtype == THINK_F32 ? 4 : 2; }
 // that both always agree.
 // ---------------------------------------------------------------------------
 struct ScoreGeom {
-    int nvec;        // 16-byte vectors per token row (Hkv*D*e/16)
-    int ncg;         // column groups of <= 256 vectors
-    int tpw;         // tokens per workgroup
-    int nsplit;      // token splits per sequence
-    size_t ws_bytes; // fp32 partials [B][nsplit][Hkv*D]
+    int nvec;          // 16-byte vectors per token row (Hkv*D*e/16)
+    int ncg;           // column groups of <= 256 vectors
+    int tpw;           // tokens per workgroup
+    int nsplit;        // token splits per sequence
+    size_t ws_bytes;   // fp32 partials [B][nsplit][Hkv*D]
 };
 ScoreGeom score_geom(const think_dims& d);
 
@@ -99,7 +99,8 @@ CompactGeom compact_geom(const think_dims& d, int keep);
 // ---------------------------------------------------------------------------
 hipError_t launch_score(const think_dims& d, const ScoreGeom& g, const void* k_cache,
                         const int32_t* seq_lens, const void* q_obs, int W, float* scores,
-                        float* partials, hipStream_t s);
+                        void* workspace, int keep, int32_t* kept_idx, int32_t* near_tie,
+                        hipStream_t s);   // kept_idx NULL: scores only
 hipError_t launch_select(const think_dims& d, const float* scores, int keep, int32_t* kept_idx,
                          int32_t* near_tie, hipStream_t s);
 hipError_t launch_compact(const think_dims& d, const CompactGeom& g, const void* k_cache,

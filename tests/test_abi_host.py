@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_header_declarations_are_all_exported(L):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     assert sorted(L.EXPORTS) == names
     so = ctypes.CDLL(L.LIB_PATH)
     for n in names:
@@ -130,6 +130,14 @@ def test_null_keep_window_workspace_and_alignment(L):
     assert lib.think_decode_attn_combine(ctypes.byref(d), FAKE, 8, FAKE, FAKE, 16, None) == -6
     assert lib.think_decode_attn_combine(ctypes.byref(dims(L, Hq=30)), FAKE, 8, FAKE, FAKE, big,
                                          None) == -2
+    assert lib.think_score_select(ctypes.byref(d), FAKE, FAKE, FAKE, 32, 0, FAKE, FAKE, None, FAKE,
+                                  big, None) == -3
+    assert lib.think_score_select(ctypes.byref(d), FAKE, FAKE, FAKE, 32, 8, None, None, None, FAKE,
+                                  big, None) == -1
+    assert lib.think_score_select(ctypes.byref(d), FAKE, FAKE, FAKE, 0, 8, None, FAKE, None, FAKE,
+                                  big, None) == -2
+    assert lib.think_score_select(ctypes.byref(d), FAKE, FAKE, FAKE, 32, 8, None, FAKE, None, FAKE,
+                                  16, None) == -6
 
 
 def test_status_strings(L):

@@ -40,6 +40,10 @@ def run_path(L, keep, q, scale):
     qd = to_dev(q)
     scores = qdk.think_score(k, lens, qo)
     idx, tie = qdk.think_select(scores, keep)
+    # the fused entry point must give the same bits
+    s2, i2, t2 = qdk.think_score_select(k, lens, qo, keep)
+    assert torch.equal(scores.view(torch.int32), s2.view(torch.int32))
+    assert torch.equal(idx, i2) and torch.equal(tie, t2)
     B, S, Hkv, D = k.shape
     thin = torch.full((B, S, Hkv, keep), float("nan"), dtype=k.dtype, device=k.device)
     qdk.think_compact_k(k, lens, idx, k_thin=thin)
