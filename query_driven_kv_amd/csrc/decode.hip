@@ -117,44 +117,51 @@ __global__ __launch_bounds__(kThreads) void k_decode_partial(
 }
 
 // Merge the chunks of one (b, h).  The block is D x SG threads: sub-group sg
-// merges a contiguous range of chunks in ascending order, eight at a time
-// with a running maximum, then the SG results are merged in ascending sg order.  Fixed order,
-// so the result is bitwise reproducible.
+// merges a contiguous range of the nsplit chunk slots in ascending order,
+// eight at a time with a running maximum, then the SG results are merged in
+// ascending sg order.  Fixed order, so the result is bitwise reproducible.
+// The ranges are fixed by nsplit rather than by the length, so the record
+// loads do not wait for the length load; slots at or past the sequence's
+// chunk count are dropped after loading (their contents are never used).
 template <int DT>
 __global__ __launch_bounds__(1024) void k_decode_combine(
         const float* __restrict__ partials, const int32_t* __restrict__ seq_lens, int s_cap,
         int chunk, int nsplit, int rec, int D, int sg_count, typename Elem<DT>::T* __restrict__ out) {
     using E = Elem<DT>;
+    constexpr float kNone = -3.402823466e38f;   // finite stand-in for an empty maximum
     const int h = blockIdx.x, b = blockIdx.y, Hq = gridDim.x;
     const int tid = threadIdx.x;
     const int d = tid % D, sg = tid / D;
-    const int len = clamp_len(seq_lens, b, s_cap);
-    const int ns = (len + chunk - 1) / chunk;
     const float* base = partials + ((size_t)b * Hq + h) * nsplit * rec;
-    const int lo = (int)((int64_t)sg * ns / sg_count), hi = (int)((int64_t)(sg + 1) * ns / sg_count);
-    // records are loaded eight at a time before they are merged, so their
-    // loads overlap instead of each waiting on the previous merge step
-    float M = -INFINITY, L = 0.0f, O = 0.0f;
+    // sg_count <= 16 and nsplit <= 2^21, so 32-bit products suffice
+    const int lo = (int)((unsigned)(sg * nsplit) / (unsigned)sg_count);
+    const int hi = (int)((unsigned)((sg + 1) * nsplit) / (unsigned)sg_count);
+    int len_raw = seq_lens[b];
+    float M = kNone, L = 0.0f, O = 0.0f;
     for (int s0 = lo; s0 < hi; s0 += 8) {
         float mv[8], lv[8], ov[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            const int s = s0 + k;
-            if (s < hi) {
-                const float* r = base + (size_t)s * rec;
-                mv[k] = r[0];
-                lv[k] = r[1];
-                ov[k] = r[4 + d];
-            } else {
-                mv[k] = -INFINITY;
-                lv[k] = 0.0f;
-                ov[k] = 0.0f;
-            }
+            const float* r = base + (size_t)min(s0 + k, nsplit - 1) * rec;
+            mv[k] = r[0];
+            lv[k] = r[1];
+            ov[k] = r[4 + d];
+        }
+        // the record loads above are issued before the length is waited on
+        asm volatile("" : "+s"(len_raw)::"memory");
+        const int len = len_raw < 0 ? 0 : (len_raw > s_cap ? s_cap : len_raw);
+        const int ns = (len + chunk - 1) / chunk;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const bool ok = s0 + k < hi && s0 + k < ns;
+            mv[k] = ok ? mv[k] : kNone;
+            lv[k] = ok ? lv[k] : 0.0f;
+            ov[k] = ok ? ov[k] : 0.0f;
         }
         float Mn = M;
 #pragma unroll
         for (int k = 0; k < 8; ++k) Mn = fmaxf(Mn, mv[k]);
-        const float f = expf(M - Mn);            // M = -inf on the first batch: f = 0
+        const float f = expf(M - Mn);
         L *= f;
         O *= f;
 #pragma unroll
@@ -175,17 +182,13 @@ __global__ __launch_bounds__(1024) void k_decode_combine(
     if (sg == 0) {
         float MM = sM[0];
         for (int r = 1; r < sg_count; ++r) MM = fmaxf(MM, sM[r]);
-        float res = 0.0f;
-        if (ns > 0) {
-            float LL = 0.0f, OO = 0.0f;
-            for (int r = 0; r < sg_count; ++r) {
-                const float f = sL[r] > 0.0f ? expf(sM[r] - MM) : 0.0f;
-                LL = fmaf(f, sL[r], LL);
-                OO = fmaf(f, sO[r * D + d], OO);
-            }
-            res = OO / LL;
+        float LL = 0.0f, OO = 0.0f;
+        for (int r = 0; r < sg_count; ++r) {
+            const float f = sL[r] > 0.0f ? expf(sM[r] - MM) : 0.0f;
+            LL = fmaf(f, sL[r], LL);
+            OO = fmaf(f, sO[r * D + d], OO);
         }
-        E::store(out, ((size_t)b * Hq + h) * D + d, res);
+        E::store(out, ((size_t)b * Hq + h) * D + d, LL > 0.0f ? OO / LL : 0.0f);
     }
 }
 

@@ -239,11 +239,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode_mfma(
         const int32_t* __restrict__ kept_idx, int s_cap, int Hkv, int G, int keep, float scale,
         int chunk, int nsplit, int rec, float* __restrict__ partials) {
     const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
-    const int len = clamp_len(seq_lens, b, s_cap);
-    const int t0 = split * chunk;
     const int tid = threadIdx.x;
     const int Hq = Hkv * G;
-    if (t0 >= len) return;                       // the combine stops before this chunk
+    const int t0 = split * chunk;
     const int lane = tid & 63, wave = tid >> 6;
     const int n16 = lane & 15, q4 = lane >> 4;
 
@@ -251,21 +249,39 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode_mfma(
     __shared__ float s_o[kWaves * 16 * kD];      // per-wave O [w][g][d]
     __shared__ float s_m[kWaves * 16], s_l[kWaves * 16];
 
-    for (int i = tid; i < 16 * KB * 32; i += kThreads) {
-        const int g = i / (KB * 32), j = i - g * (KB * 32);
-        uint16_t val = 0;
-        if (g < G && j < keep) {
-            int c = kept_idx[((size_t)b * Hkv + kv) * keep + j];
-            c = c < 0 ? 0 : (c >= kD ? kD - 1 : c);
-            val = q[((size_t)b * Hq + kv * G + g) * kD + c];
-        }
-        s_q[g * kD + j] = val;
-    }
-    __syncthreads();
-    uint4 qB[KB];                                // B operand: lane holds qS[jb*32+8*q4+i][g=n16]
+    // Prologue, ordered so the stream starts after one memory round trip:
+    // the sequence length and this thread's kept-channel indices are loaded
+    // together; then the query elements they name and the first two steps'
+    // K_thin/V fragments are issued back to back, and only then does the
+    // workgroup wait for the query to build the MFMA operand.
+    constexpr int kGather = 16 * KB * 32 / kThreads;
+    const int len_raw = seq_lens[b];
+    // The gather reads through buffer descriptors bounded to this kv head's
+    // kept indices and its G query rows: slots past keep or past G read zero
+    // in hardware, so every load is unconditional and none waits on another.
+    // A chunk that starts past the length still runs (all its stream loads
+    // are empty) and writes a record the combine never reads; an early exit
+    // here would put the length load in front of the gather.
+    const auto rsrc_idx = make_rsrc(kept_idx + ((size_t)b * Hkv + kv) * keep, (uint32_t)keep * 4u);
+    const auto rsrc_q = make_rsrc(q + ((size_t)b * Hq + (size_t)kv * G) * kD, (uint32_t)(G * kD * 2));
+    int cidx[kGather];
 #pragma unroll
-    for (int jb = 0; jb < KB; ++jb)
-        qB[jb] = *reinterpret_cast<const uint4*>(&s_q[n16 * kD + jb * 32 + 8 * q4]);
+    for (int r = 0; r < kGather; ++r) {
+        const int j = (tid + r * kThreads) % (KB * 32);
+        cidx[r] = __builtin_amdgcn_raw_buffer_load_b32(rsrc_idx, j * 4, 0, 0);
+    }
+    // both loads are in flight before either is waited on
+    asm volatile("" ::"s"(len_raw), "v"(cidx[0]));
+    const int len = len_raw < 0 ? 0 : (len_raw > s_cap ? s_cap : len_raw);
+    uint16_t qv[kGather];
+#pragma unroll
+    for (int r = 0; r < kGather; ++r) {
+        const int i = tid + r * kThreads;
+        const int g = i / (KB * 32), j = i - g * (KB * 32);
+        const int c = cidx[r] < 0 ? 0 : (cidx[r] >= kD ? kD - 1 : cidx[r]);
+        const int off = j < keep ? (g * kD + c) * 2 : (int)kOff;
+        qv[r] = __builtin_amdgcn_raw_buffer_load_b16(rsrc_q, off, 0, 0);
+    }
 
     const int tw = chunk / kWaves;
     const int ws = t0 + __builtin_amdgcn_readfirstlane(wave) * tw;   // wave-uniform
@@ -277,7 +293,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode_mfma(
     // at token ts end at the last valid token's row
     const uint16_t* kw = k_thin + ((size_t)b * s_cap + ws) * kt_row + (size_t)kv * keep;
     const uint16_t* vw = v_cache + ((size_t)b * s_cap + ws) * v_row + (size_t)kv * kD;
-    // descriptors of the step starting at token ts: empty once ts >= we
+    // descriptors of the step starting at token ts: empty once ts >= we (a
+    // wave past the length issues only empty loads, which read zeros without
+    // touching memory)
     auto rsrc_k = [&](int ts) {
         const int nt = min(32, we - ts);
         const uint32_t bytes = nt > 0 ? (uint32_t)(((nt - 1) * kt_row + keep) * 2) : 0u;
@@ -289,36 +307,47 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode_mfma(
         return make_rsrc(vw + (size_t)(ts - ws) * v_row, bytes);
     };
 
+    // Two fragment buffers: the loads of step s+1 are in flight while step s
+    // computes.  Both buffers are loaded unconditionally (a step past the end
+    // has an empty descriptor), so the wait before each compute covers only
+    // that buffer's own loads.  (Rows that are not 4-byte aligned are read
+    // element by element; with three or more channel blocks a second buffer
+    // would not fit in registers, so those shapes use one.)
+    constexpr bool kTwoBuffers = KAL == 8 || KB <= 2 || (KAL == 2 && KB <= 3);
+    Frag<KB> fa;
+    [[maybe_unused]] Frag<KB> fb;
+    load_step<KB, KAL>(fa, rsrc_k(ws), rsrc_v(ws), lo);
+    if constexpr (kTwoBuffers) load_step<KB, KAL>(fb, rsrc_k(ws + 32), rsrc_v(ws + 32), lo);
+
+#pragma unroll
+    for (int r = 0; r < kGather; ++r) {
+        const int i = tid + r * kThreads;
+        const int g = i / (KB * 32), j = i - g * (KB * 32);
+        s_q[g * kD + j] = qv[r];
+    }
+    __syncthreads();
+    uint4 qB[KB];                                // B operand: lane holds qS[jb*32+8*q4+i][g=n16]
+#pragma unroll
+    for (int jb = 0; jb < KB; ++jb)
+        qB[jb] = *reinterpret_cast<const uint4*>(&s_q[n16 * kD + jb * 32 + 8 * q4]);
+
     f32x4 O[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) O[c] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, l = 0.0f;
 
-    // Two fragment buffers: the loads of step s+1 are in flight while step s
-    // computes.  Both buffers are loaded unconditionally (a step past the end
-    // has an empty descriptor and reads zeros without touching memory), so
-    // the wait before each compute covers only that buffer's own loads.
-    // (Rows that are not 4-byte aligned are read element by element; with
-    // three or more channel blocks a second buffer would not fit in
-    // registers, so those shapes use one.)
-    constexpr bool kTwoBuffers = KAL == 8 || KB <= 2 || (KAL == 2 && KB <= 3);
-    Frag<KB> fa;
-    if (ws < we) {
-        if constexpr (kTwoBuffers) {
-            Frag<KB> fb;
-            load_step<KB, KAL>(fa, rsrc_k(ws), rsrc_v(ws), lo);
-            for (int ts = ws; ts < we; ts += 64) {
-                load_step<KB, KAL>(fb, rsrc_k(ts + 32), rsrc_v(ts + 32), lo);
-                compute_step<KB>(fa, min(32, we - ts), scale, qB, q4, O, m, l);
-                load_step<KB, KAL>(fa, rsrc_k(ts + 64), rsrc_v(ts + 64), lo);
-                if (ts + 32 < we)
-                    compute_step<KB>(fb, min(32, we - ts - 32), scale, qB, q4, O, m, l);
-            }
-        } else {
-            for (int ts = ws; ts < we; ts += 32) {
-                load_step<KB, KAL>(fa, rsrc_k(ts), rsrc_v(ts), lo);
-                compute_step<KB>(fa, min(32, we - ts), scale, qB, q4, O, m, l);
-            }
+    if constexpr (kTwoBuffers) {
+        for (int ts = ws; ts < we; ts += 64) {
+            compute_step<KB>(fa, min(32, we - ts), scale, qB, q4, O, m, l);
+            load_step<KB, KAL>(fa, rsrc_k(ts + 64), rsrc_v(ts + 64), lo);
+            if (ts + 32 < we)
+                compute_step<KB>(fb, min(32, we - ts - 32), scale, qB, q4, O, m, l);
+            load_step<KB, KAL>(fb, rsrc_k(ts + 96), rsrc_v(ts + 96), lo);
+        }
+    } else {
+        for (int ts = ws; ts < we; ts += 32) {
+            compute_step<KB>(fa, min(32, we - ts), scale, qB, q4, O, m, l);
+            load_step<KB, KAL>(fa, rsrc_k(ts + 32), rsrc_v(ts + 32), lo);
         }
     }
 
