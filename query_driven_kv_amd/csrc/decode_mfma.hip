@@ -51,44 +51,6 @@ __device__ __forceinline__ f32x4 mfma(uint4 a, uint4 b, f32x4 c) {
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Buffer loads: a wave-uniform descriptor (base, size in bytes) lives in
-// SGPRs and each lane supplies a 32-bit byte offset.  An offset at or past
-// the size reads as zero in hardware, which is how tokens past the valid
-// range and channels past `keep` are masked without branches.
-constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, 32-bit data format
-constexpr int kNonTemporal = 2;                 // streaming: read once per call
-constexpr uint32_t kOff = 0x80000000u;          // an offset past any descriptor
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                             kRsrcWord3);
-}
-
-// 8 consecutive bf16 of a K_thin head row at byte offset `off` (kOff: none).
-// `mask` zeroes the channels past keep inside the last octet of a row when
-// rows are not 16-byte aligned (KAL = 2 or 1: dword or element loads).
-template <int KAL>
-__device__ __forceinline__ uint4 load_k8(__amdgpu_buffer_rsrc_t r, uint32_t off, const uint4& mask) {
-    if (KAL == 8) {
-        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kNonTemporal);
-        return make_uint4(v.x, v.y, v.z, v.w);
-    } else if (KAL == 2) {
-        uint4 v;
-        v.x = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kNonTemporal) & mask.x;
-        v.y = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(off + 4), 0, kNonTemporal) & mask.y;
-        v.z = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(off + 8), 0, kNonTemporal) & mask.z;
-        v.w = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(off + 12), 0, kNonTemporal) & mask.w;
-        return v;
-    } else {
-        uint32_t h[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            h[k] = __builtin_amdgcn_raw_buffer_load_b16(r, (int)(off + 2 * k), 0, kNonTemporal);
-        return make_uint4((h[0] | (h[1] << 16)) & mask.x, (h[2] | (h[3] << 16)) & mask.y,
-                          (h[4] | (h[5] << 16)) & mask.z, (h[6] | (h[7] << 16)) & mask.w);
-    }
-}
-
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
     return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
@@ -118,31 +80,46 @@ __device__ __forceinline__ uint4 v_column(const uint4 (&v)[8]) {
     return r;
 }
 
-template <int KB>
+// K_thin octets (8 channels, 16 bytes of one head row).  KAL = 8: head rows
+// are 16-byte aligned and an octet is one aligned dwordx4.  KAL = 2: rows are
+// 4-byte aligned; the octet is one dwordx4 at a 4-byte aligned offset and the
+// channels past keep are masked.  KAL = 1: rows are only 2-byte aligned; the
+// dwordx4 at the dword boundary at or below the octet and the dword after it
+// are loaded, and the octet is re-paired from them with a per-lane byte shift
+// (0 or 2) when the step computes.  Every case is one or two wide loads per
+// octet, never element loads.
+template <int KB, int KAL>
 struct Frag {
-    uint4 k[2][KB];   // K_thin A operands: token half x 32-channel block
-    uint4 v[8];       // V rows of this lane's 8 tokens (16 bytes each)
+    uint4 k[2][KB];                      // token half x 32-channel block
+    uint32_t ky[2][KAL == 1 ? KB : 1];   // KAL 1: the dword after each dwordx4
+    uint4 v[8];                          // V rows of this lane's 8 tokens (16 bytes each)
 };
 
 // Lane-constant parts of the loads of one 32-token step (byte offsets from
-// the step's first K_thin / V row of this kv head).
+// the step's K_thin / V descriptor bases).
 template <int KB>
 struct LaneOffsets {
-    uint32_t k[2][KB];   // K_thin octet [half][channel block]; kOff when past keep
+    uint32_t k[2][KB];   // dword-aligned offset of the octet's dwordx4; kOff when past keep
+    uint32_t ks[2][KB];  // byte shift of the octet inside that dwordx4 (KAL 1)
     uint4 kmask[KB];     // channel mask of the octet (KAL 2 / 1)
     uint32_t v[8];       // V row of this lane's token i, channel octet n16
 };
 
+// `delta` is the K_thin descriptor base's distance below the step's first
+// row of this head (0, or 2 when that row is not 4-byte aligned).
 template <int KB>
 __device__ __forceinline__ LaneOffsets<KB> lane_offsets(int keep, size_t kt_row, size_t v_row,
-                                                        int n16, int q4) {
+                                                        int n16, int q4, uint32_t delta) {
     LaneOffsets<KB> lo;
 #pragma unroll
     for (int jb = 0; jb < KB; ++jb) {
         const int j0 = jb * 32 + 8 * q4;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-            lo.k[h][jb] = j0 < keep ? (uint32_t)(((16 * h + n16) * kt_row + j0) * 2) : kOff;
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t off = (uint32_t)(((16 * h + n16) * kt_row + j0) * 2) + delta;
+            lo.ks[h][jb] = j0 < keep ? (off & 2u) : 0u;
+            lo.k[h][jb] = j0 < keep ? (off & ~3u) : kOff;
+        }
         uint32_t mw[4];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -160,29 +137,51 @@ __device__ __forceinline__ LaneOffsets<KB> lane_offsets(int keep, size_t kt_row,
 // Issue the loads of one 32-token step: rk / rv cover this kv head's rows of
 // the step's valid tokens only, so every other read returns zero.
 template <int KB, int KAL>
-__device__ __forceinline__ void load_step(Frag<KB>& f, __amdgpu_buffer_rsrc_t rk,
+__device__ __forceinline__ void load_step(Frag<KB, KAL>& f, __amdgpu_buffer_rsrc_t rk,
                                           __amdgpu_buffer_rsrc_t rv, const LaneOffsets<KB>& lo) {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int jb = 0; jb < KB; ++jb) f.k[h][jb] = load_k8<KAL>(rk, lo.k[h][jb], lo.kmask[jb]);
+        for (int jb = 0; jb < KB; ++jb) {
+            f.k[h][jb] = ldb_stream(rk, lo.k[h][jb]);
+            if constexpr (KAL == 1)
+                f.ky[h][jb] = __builtin_amdgcn_raw_buffer_load_b32(rk, (int)(lo.k[h][jb] + 16u), 0,
+                                                                   kNonTemporal);
+        }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)lo.v[i], 0, kNonTemporal);
-        f.v[i] = make_uint4(x.x, x.y, x.z, x.w);
+    for (int i = 0; i < 8; ++i) f.v[i] = ldb_stream(rv, lo.v[i]);
+}
+
+// The logits' A operand for one octet, from the loaded words.
+template <int KB, int KAL>
+__device__ __forceinline__ uint4 k_operand(const Frag<KB, KAL>& f, const LaneOffsets<KB>& lo,
+                                           int h, int jb) {
+    const uint4 x = f.k[h][jb];
+    if constexpr (KAL == 8) {
+        return x;
+    } else if constexpr (KAL == 2) {
+        const uint4 mk = lo.kmask[jb];
+        return make_uint4(x.x & mk.x, x.y & mk.y, x.z & mk.z, x.w & mk.w);
+    } else {
+        const uint4 mk = lo.kmask[jb];
+        const uint32_t sh = lo.ks[h][jb];
+        return make_uint4(__builtin_amdgcn_alignbyte(x.y, x.x, sh) & mk.x,
+                          __builtin_amdgcn_alignbyte(x.z, x.y, sh) & mk.y,
+                          __builtin_amdgcn_alignbyte(x.w, x.z, sh) & mk.z,
+                          __builtin_amdgcn_alignbyte(f.ky[h][jb], x.w, sh) & mk.w);
     }
 }
 
 // Logits, online softmax and the value product of one 32-token step.
-template <int KB>
-__device__ __forceinline__ void compute_step(const Frag<KB>& f, int nt, float scale,
-                                             const uint4 (&qB)[KB], int q4, f32x4 (&O)[8],
-                                             float& m, float& l) {
+template <int KB, int KAL>
+__device__ __forceinline__ void compute_step(const Frag<KB, KAL>& f, const LaneOffsets<KB>& lo,
+                                             int nt, float scale, const uint4 (&qB)[KB], int q4,
+                                             f32x4 (&O)[8], float& m, float& l) {
     f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int jb = 0; jb < KB; ++jb) {
-        c0 = mfma(f.k[0][jb], qB[jb], c0);
-        c1 = mfma(f.k[1][jb], qB[jb], c1);
+        c0 = mfma(k_operand<KB, KAL>(f, lo, 0, jb), qB[jb], c0);
+        c1 = mfma(k_operand<KB, KAL>(f, lo, 1, jb), qB[jb], c1);
     }
     // c0[r]: token 4*q4 + r of the step, c1[r]: token 16 + 4*q4 + r (nt of
     // the 32 are valid); head g = lane % 16
@@ -288,18 +287,26 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode_mfma(
     const int we = min(ws + tw, len);
     const size_t kt_row = (size_t)Hkv * keep;
     const size_t v_row = (size_t)Hkv * kD;
-    const LaneOffsets<KB> lo = lane_offsets<KB>(keep, kt_row, v_row, n16, q4);
     // this wave's first rows of kv head kv; the valid bytes of a step starting
-    // at token ts end at the last valid token's row
+    // at token ts end at the last valid token's row.  Steps advance by a
+    // multiple of 4 bytes, so a K_thin row that is not 4-byte aligned (odd
+    // keep) is off by the same 2 bytes in every step: the descriptor base
+    // starts `delta` bytes below it.
     const uint16_t* kw = k_thin + ((size_t)b * s_cap + ws) * kt_row + (size_t)kv * keep;
     const uint16_t* vw = v_cache + ((size_t)b * s_cap + ws) * v_row + (size_t)kv * kD;
+    const uint32_t delta = KAL == 1 ? (uint32_t)(reinterpret_cast<uintptr_t>(kw) & 3u) : 0u;
+    const LaneOffsets<KB> lo = lane_offsets<KB>(keep, kt_row, v_row, n16, q4, delta);
     // descriptors of the step starting at token ts: empty once ts >= we (a
     // wave past the length issues only empty loads, which read zeros without
     // touching memory)
     auto rsrc_k = [&](int ts) {
         const int nt = min(32, we - ts);
-        const uint32_t bytes = nt > 0 ? (uint32_t)(((nt - 1) * kt_row + keep) * 2) : 0u;
-        return make_rsrc(kw + (size_t)(ts - ws) * kt_row, bytes);
+        // a dword reads as zero unless it ends inside the range, so the range
+        // is rounded up to whole dwords (the extra bytes share the last valid
+        // dword and are masked)
+        const uint32_t bytes =
+                nt > 0 ? ((uint32_t)(((nt - 1) * kt_row + keep) * 2) + delta + 3u) & ~3u : 0u;
+        return make_rsrc(reinterpret_cast<const char*>(kw + (size_t)(ts - ws) * kt_row) - delta, bytes);
     };
     auto rsrc_v = [&](int ts) {
         const int nt = min(32, we - ts);
@@ -310,14 +317,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode_mfma(
     // Two fragment buffers: the loads of step s+1 are in flight while step s
     // computes.  Both buffers are loaded unconditionally (a step past the end
     // has an empty descriptor), so the wait before each compute covers only
-    // that buffer's own loads.  (Rows that are not 4-byte aligned are read
-    // element by element; with three or more channel blocks a second buffer
-    // would not fit in registers, so those shapes use one.)
-    constexpr bool kTwoBuffers = KAL == 8 || KB <= 2 || (KAL == 2 && KB <= 3);
-    Frag<KB> fa;
-    [[maybe_unused]] Frag<KB> fb;
+    // that buffer's own loads.
+    Frag<KB, KAL> fa, fb;
     load_step<KB, KAL>(fa, rsrc_k(ws), rsrc_v(ws), lo);
-    if constexpr (kTwoBuffers) load_step<KB, KAL>(fb, rsrc_k(ws + 32), rsrc_v(ws + 32), lo);
+    load_step<KB, KAL>(fb, rsrc_k(ws + 32), rsrc_v(ws + 32), lo);
 
 #pragma unroll
     for (int r = 0; r < kGather; ++r) {
@@ -336,19 +339,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode_mfma(
     for (int c = 0; c < 8; ++c) O[c] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, l = 0.0f;
 
-    if constexpr (kTwoBuffers) {
-        for (int ts = ws; ts < we; ts += 64) {
-            compute_step<KB>(fa, min(32, we - ts), scale, qB, q4, O, m, l);
-            load_step<KB, KAL>(fa, rsrc_k(ts + 64), rsrc_v(ts + 64), lo);
-            if (ts + 32 < we)
-                compute_step<KB>(fb, min(32, we - ts - 32), scale, qB, q4, O, m, l);
-            load_step<KB, KAL>(fb, rsrc_k(ts + 96), rsrc_v(ts + 96), lo);
-        }
-    } else {
-        for (int ts = ws; ts < we; ts += 32) {
-            compute_step<KB>(fa, min(32, we - ts), scale, qB, q4, O, m, l);
-            load_step<KB, KAL>(fa, rsrc_k(ts + 32), rsrc_v(ts + 32), lo);
-        }
+    for (int ts = ws; ts < we; ts += 64) {
+        compute_step<KB, KAL>(fa, lo, min(32, we - ts), scale, qB, q4, O, m, l);
+        load_step<KB, KAL>(fa, rsrc_k(ts + 64), rsrc_v(ts + 64), lo);
+        if (ts + 32 < we)
+            compute_step<KB, KAL>(fb, lo, min(32, we - ts - 32), scale, qB, q4, O, m, l);
+        load_step<KB, KAL>(fb, rsrc_k(ts + 96), rsrc_v(ts + 96), lo);
     }
 
     // ---- merge the 4 waves (a wave past len_b has m = -inf, l = 0, O = 0)

@@ -59,6 +59,24 @@ __device__ __forceinline__ uint4 ldg_stream(const void* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Buffer loads: a wave-uniform descriptor (base, size in bytes) lives in
+// SGPRs and each lane supplies a 32-bit byte offset.  An offset at or past
+// the size reads as zero in hardware, so ranges are masked without branches
+// (a load behind a branch makes the compiler drain every load in flight at
+// the join).
+constexpr int kRsrcWord3 = 0x00020000;          // raw buffer, 32-bit data format
+constexpr int kNonTemporal = 2;                 // streaming: read once per call
+constexpr uint32_t kOff = 0x80000000u;          // an offset past any descriptor
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             kRsrcWord3);
+}
+__device__ __forceinline__ uint4 ldb_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kNonTemporal);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ int clamp_len(const int32_t* seq_lens, int b, int s_cap) {
     int n = seq_lens[b];
     return n < 0 ? 0 : (n > s_cap ? s_cap : n);
