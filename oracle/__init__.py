@@ -48,6 +48,7 @@ def _load():
     lib.oracle_select.argtypes = [i32, i32, i32, vp, i32, vp, vp]
     lib.oracle_compact.argtypes = [i32] * 5 + [vp, vp, vp, i32, vp]
     lib.oracle_decode.argtypes = [i32] * 6 + [vp, vp, vp, vp, vp, i32, dbl, vp]
+    lib.oracle_append.argtypes = [i32] * 5 + [vp, vp, vp, vp, i32, vp, vp]
     lib.oracle_full_attn.argtypes = [i32] * 6 + [vp, vp, vp, vp, dbl, vp]
     lib.oracle_residual_materialised.argtypes = [i32, i32, i32, vp, vp, vp]
     lib.oracle_residual_materialised.restype = dbl
@@ -151,6 +152,25 @@ def compact(k_cache, seq_lens, kept_idx, fill=None):
     _check(_load().oracle_compact(B, S, Hkv, D, _dtype_code(k_cache), _ptr(k_cache), _ptr(lens),
                                   _ptr(idx), keep, _ptr(out)), "compact")
     return out
+
+
+def append(k_new, v_new, seq_lens, kept_idx, k_thin, v_cache):
+    """Decode-time append: for every b with len_b < S_cap, write the pruned new
+    key K_thin[b,len_b,kv,j] = k_new[b,kv,kept_idx[b,kv,j]] and the new value
+    V[b,len_b,kv,:] = v_new[b,kv,:], then len_b += 1.  Returns new copies
+    (k_thin, v_cache, seq_lens); the inputs are not modified."""
+    k_new, v_new = _c(k_new), _c(v_new)
+    idx = _c(kept_idx, np.int32)
+    kt, vc = np.array(k_thin, copy=True), np.array(v_cache, copy=True)
+    lens = np.array(seq_lens, dtype=np.int32, copy=True)
+    B, S, Hkv, D = vc.shape
+    keep = idx.shape[-1]
+    if (k_new.shape != (B, Hkv, D) or v_new.shape != (B, Hkv, D) or kt.shape != (B, S, Hkv, keep)
+            or k_new.dtype != vc.dtype or kt.dtype != vc.dtype or v_new.dtype != vc.dtype):
+        raise ValueError("shape or dtype mismatch")
+    _check(_load().oracle_append(B, S, Hkv, D, _dtype_code(vc), _ptr(k_new), _ptr(v_new),
+                                 _ptr(lens), _ptr(idx), keep, _ptr(kt), _ptr(vc)), "append")
+    return kt, vc, lens
 
 
 def decode(q, k_thin, v_cache, seq_lens, kept_idx, scale):

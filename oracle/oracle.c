@@ -288,6 +288,48 @@ int oracle_compact(int B, int S_cap, int Hkv, int D, int dtype, const void *k_ca
 }
 
 /* ---------------------------------------------------------------------------
+ * Decode-time append (the step after the path): inference continues on the
+ * pruned cache ("ThinK: Thinner Key Cache by Query-Driven Pruning", Method
+ * details -> Technical framework, last step), so a generated token's key is
+ * stored pruned with the same kept set as the cached keys, and its value in
+ * full.  For every b with len_b < S_cap:
+ *   K_thin[b,len_b,kv,j] = k_new[b,kv,kept_idx[b,kv,j]]
+ *   V[b,len_b,kv,:]      = v_new[b,kv,:]
+ *   len_b               += 1
+ * A sequence already at capacity is left as it is.  Byte copies.
+ * Layouts: k_new, v_new [B,Hkv,D]; K_thin [B,S_cap,Hkv,keep]; V [B,S_cap,Hkv,D].
+ * ------------------------------------------------------------------------- */
+int oracle_append(int B, int S_cap, int Hkv, int D, int dtype, const void *k_new,
+                  const void *v_new, int32_t *seq_lens, const int32_t *kept_idx, int keep,
+                  void *k_thin, void *v_cache) {
+    if (!dims_ok(B, S_cap, Hkv, Hkv, D, dtype) || keep < 1 || keep > D) return -1;
+    if (!k_new || !v_new || !seq_lens || !kept_idx || !k_thin || !v_cache) return -1;
+    if (!lens_ok(B, S_cap, seq_lens)) return -1;
+    for (size_t i = 0; i < (size_t)B * Hkv * keep; ++i)
+        if (kept_idx[i] < 0 || kept_idx[i] >= D) return -1;
+    const size_t es = elem_size(dtype);
+    const unsigned char *kn = (const unsigned char *)k_new;
+    const unsigned char *vn = (const unsigned char *)v_new;
+    unsigned char *kt = (unsigned char *)k_thin;
+    unsigned char *vc = (unsigned char *)v_cache;
+    for (int b = 0; b < B; ++b) {
+        const int t = seq_lens[b];
+        if (t >= S_cap) continue;
+        for (int kv = 0; kv < Hkv; ++kv) {
+            const int32_t *idx = kept_idx + ((size_t)b * Hkv + kv) * keep;
+            const size_t src = ((size_t)b * Hkv + kv) * D;
+            const size_t krow = (((size_t)b * S_cap + t) * Hkv + kv) * keep;
+            const size_t vrow = (((size_t)b * S_cap + t) * Hkv + kv) * D;
+            for (int j = 0; j < keep; ++j)
+                memcpy(kt + (krow + j) * es, kn + (src + idx[j]) * es, es);
+            memcpy(vc + vrow * es, vn + src * es, (size_t)D * es);
+        }
+        seq_lens[b] = t + 1;
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
  * Stage (d): decode attention on the pruned key cache, per (b, q head h),
  * with kv = h / G:
  *   qS[j] = q[b,h,kept_idx[b,kv,j]]

@@ -393,3 +393,85 @@ def test_decode_special_cases():
     q2[0, :, 1] = np.float32(2000.0)          # channel 1 is kept as j=0
     o = oracle.decode(q2, thin2, v, [16], idx, 1.0)
     np.testing.assert_array_equal(o[0, 0], vf[0, 9, 0])
+
+
+# --------------------------------------------------------------------------- decode-time append
+def _append_case(seed, dtype, B=3, Hq=4, Hkv=2, D=16, S=12, lens=(5, 11, 12), keep=6):
+    cfg, L = _case(seed, B=B, Hq=Hq, Hkv=Hkv, D=D, S=S, dtype=dtype, lens=list(lens))
+    s = oracle.score(L["k_cache"], L["seq_lens"], L["q_obs"])
+    idx, _ = oracle.select(s, keep)
+    rng = np.random.default_rng(seed)
+    sd = kvsynth.storage_dtype(dtype)
+    if dtype == "f32":
+        k_new = rng.standard_normal((B, Hkv, D)).astype(np.float32)
+        v_new = rng.standard_normal((B, Hkv, D)).astype(np.float32)
+    else:
+        k_new = kvsynth.to_bf16_bits(rng.standard_normal((B, Hkv, D)).astype(np.float32))
+        v_new = kvsynth.to_bf16_bits(rng.standard_normal((B, Hkv, D)).astype(np.float32))
+    assert k_new.dtype == sd
+    return cfg, L, idx, k_new, v_new
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_append_equals_compaction_of_the_extended_cache(dtype):
+    """The appended thin row is what compacting the cache with the new key in
+    row len_b gives; earlier rows and the other sequences are untouched, and a
+    full sequence is left as it is."""
+    cfg, L, idx, k_new, v_new = _append_case(21, dtype)
+    lens = L["seq_lens"]
+    thin = oracle.compact(L["k_cache"], lens, idx)
+    kt, vc, lens2 = oracle.append(k_new, v_new, lens, idx, thin, L["v_cache"])
+    S = L["k_cache"].shape[1]
+    ext_k = L["k_cache"].copy()
+    for b, n in enumerate(lens):
+        if n < S:
+            ext_k[b, n] = k_new[b]
+    ref = oracle.compact(ext_k, np.minimum(lens + 1, S), idx)
+    for b, n in enumerate(lens):
+        m = min(n + 1, S)
+        assert lens2[b] == m
+        np.testing.assert_array_equal(kt[b, :m].view(np.uint8), ref[b, :m].view(np.uint8))
+        np.testing.assert_array_equal(kt[b, m:].view(np.uint8), thin[b, m:].view(np.uint8))
+        if n < S:
+            np.testing.assert_array_equal(vc[b, n].view(np.uint8), v_new[b].view(np.uint8))
+        np.testing.assert_array_equal(np.delete(vc[b], n, axis=0).view(np.uint8) if n < S
+                                      else vc[b].view(np.uint8),
+                                      np.delete(L["v_cache"][b], n, axis=0).view(np.uint8) if n < S
+                                      else L["v_cache"][b].view(np.uint8))
+    # the inputs were not modified
+    np.testing.assert_array_equal(lens, L["seq_lens"])
+
+
+def test_decode_after_append_keep_all_equals_unpruned_attention():
+    """At keep = D, decoding over the appended pruned cache is exactly
+    unpruned attention over the cache extended by the new key and value."""
+    cfg, L, _, k_new, v_new = _append_case(22, "f32", keep=16)
+    idx = np.broadcast_to(np.arange(16, dtype=np.int32), (3, 2, 16)).copy()
+    lens = L["seq_lens"]
+    thin = oracle.compact(L["k_cache"], lens, idx)
+    kt, vc, lens2 = oracle.append(k_new, v_new, lens, idx, thin, L["v_cache"])
+    ext_k = L["k_cache"].copy()
+    for b, n in enumerate(lens):
+        if n < ext_k.shape[1]:
+            ext_k[b, n] = k_new[b]
+    q = kvsynth.decode_q(cfg, 22, 0)
+    a = oracle.decode(q, kt, vc, lens2, idx, 0.3)
+    b = oracle.full_attn(q, ext_k, vc, lens2, 0.3)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_decode_after_append_attends_to_the_new_token():
+    """A new key whose logit exceeds every cached one by more than 800 takes all
+    the attention weight: the output is the new value row exactly."""
+    cfg, L, idx, k_new, v_new = _append_case(23, "f32", B=1, lens=(7,), Hq=2, Hkv=1)
+    thin = oracle.compact(L["k_cache"], L["seq_lens"], idx)
+    q = np.zeros((1, 2, 16), np.float32)
+    c0 = int(idx[0, 0, 0])
+    q[0, :, c0] = 1.0
+    thin[0, :7] = 0                                  # cached logits 0
+    k_new = np.zeros_like(k_new)
+    k_new[0, 0, c0] = 1000.0                         # new logit 1000 at scale 1
+    kt, vc, lens2 = oracle.append(k_new, v_new, L["seq_lens"], idx, thin, L["v_cache"])
+    o = oracle.decode(q, kt, vc, lens2, idx, 1.0)
+    np.testing.assert_array_equal(o[0, 0], v_new[0, 0].astype(np.float64))
+    np.testing.assert_array_equal(o[0, 1], v_new[0, 0].astype(np.float64))
