@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define THINK_ABI_VERSION 1
+#define THINK_ABI_VERSION 2
 
 #ifndef THINK_API
 #define THINK_API __attribute__((visibility("default")))
@@ -186,6 +186,27 @@ THINK_API int think_decode_attn_partial(const think_dims *d, const void *q, cons
 THINK_API int think_decode_attn_combine(const think_dims *d, const int32_t *seq_lens, int32_t keep,
                                         void *out, const void *workspace, size_t workspace_bytes,
                                         void *stream);
+
+/*
+ * Decode-time append, the step after stage (d): inference continues on the
+ * pruned cache ("ThinK", Technical framework, last step), so a generated
+ * token's key is stored pruned with the kept set already chosen for its
+ * (b, kv), and its value in full.  For every b with len_b < S_cap:
+ *   k_thin[b,len_b,kv,j]  = k_new[b,kv,kept_idx[b,kv,j]]
+ *   v_cache[b,len_b,kv,:] = v_new[b,kv,:]
+ *   seq_lens[b]           = len_b + 1        (device memory, updated in place)
+ * A sequence already at S_cap is left as it is (no row written, length
+ * kept); the caller owns capacity.  A think_decode_attn that follows on the
+ * same stream attends over len_b + 1 tokens, the new one included.
+ *   k_new, v_new  [B,Hkv,D] dtype
+ *   seq_lens      int32 [B], read and written
+ *   k_thin        [B,S_cap,Hkv,keep] dtype, row len_b written
+ *   v_cache       [B,S_cap,Hkv,D] dtype, row len_b written
+ * kept_idx entries outside [0, D) are clamped into range.  A byte copy.
+ */
+THINK_API int think_append_kv(const think_dims *d, const void *k_new, const void *v_new,
+                              int32_t *seq_lens, const int32_t *kept_idx, int32_t keep,
+                              void *k_thin, void *v_cache, void *stream);
 
 /* Static description of a status code. */
 THINK_API const char *think_status_string(int status);

@@ -17,7 +17,7 @@ channels and a rank-32 component plus small noise; values are N(0, 1).
 Spawn keys: (config id, layer, tensor id, sub-index) with tensor ids
   0 channel scales, 1 outlier picks, 2 low-rank factor U, 3 low-rank basis W_r,
   4 key noise, 5 observation-window queries, 6 values, 7 ragged lengths,
-  100+s decode query of step s.
+  100+s decode query of step s, 200+s and 300+s the key and value that step appends.
 """
 from __future__ import annotations
 
@@ -226,6 +226,18 @@ def decode_q(cfg: Config, layer: int, step: int, scale: Optional[np.ndarray] = N
     head_scale = np.repeat(scale, cfg.group, axis=0)
     x = _normal(_rng(cfg, layer, 100 + step), (cfg.batch, cfg.n_q_heads, cfg.head_dim))
     return _store(x * head_scale, cfg.dtype)
+
+
+def decode_kv(cfg: Config, layer: int, step: int, scale: Optional[np.ndarray] = None):
+    """The key and value a decode step appends: [B,Hkv,D] each; the key is
+    N(0,1) times the layer's channel scale (tensor id 200+step), the value
+    N(0,1) (tensor id 300+step)."""
+    if scale is None:
+        scale = channel_scale(cfg, layer)
+    shape = (cfg.batch, cfg.n_kv_heads, cfg.head_dim)
+    k = _normal(_rng(cfg, layer, 200 + step), shape) * scale
+    v = _normal(_rng(cfg, layer, 300 + step), shape)
+    return _store(k, cfg.dtype), _store(v, cfg.dtype)
 
 
 def as_float(a: np.ndarray) -> np.ndarray:

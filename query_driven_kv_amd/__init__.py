@@ -19,7 +19,7 @@ from ._lib import THINK_BF16, THINK_F32, ThinkError, think_dims
 
 __all__ = ["think_score", "think_score_select", "think_select", "think_compact_k",
            "think_decode_attn",
-           "think_decode_attn_partial", "think_decode_attn_combine",
+           "think_decode_attn_partial", "think_decode_attn_combine", "think_append_kv",
            "think_keep_from_ratio", "think_score_workspace_bytes", "think_decode_workspace_bytes",
            "think_abi_version", "make_dims", "ThinkError", "think_dims", "LIB_PATH"]
 
@@ -223,3 +223,23 @@ def think_decode_attn_combine(dims, keep, seq_lens, workspace, out, *, stream=No
         ctypes.byref(dims), _p(seq_lens), int(keep), _p(out), _p(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
+
+
+def think_append_kv(k_new, v_new, seq_lens, kept_idx, k_thin, v_cache, *, stream=None):
+    """Decode-time append.  k_new, v_new [B,Hkv,D]; writes the pruned key into
+    k_thin[b, len_b] and the value into v_cache[b, len_b] and advances
+    seq_lens[b] in place (a full sequence is left as it is).  Returns seq_lens."""
+    _dev(k_new, v_new, seq_lens, kept_idx, k_thin, v_cache)
+    _i32(seq_lens, "seq_lens")
+    _i32(kept_idx, "kept_idx")
+    B, S, Hkv, D = v_cache.shape
+    keep = kept_idx.shape[-1]
+    if (tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D)
+            or tuple(k_thin.shape) != (B, S, Hkv, keep) or tuple(kept_idx.shape) != (B, Hkv, keep)
+            or len({k_new.dtype, v_new.dtype, k_thin.dtype, v_cache.dtype}) != 1):
+        raise ValueError("shape or dtype mismatch between k_new, v_new, k_thin, v_cache, kept_idx")
+    dims = make_dims(B, Hkv, Hkv, D, S, _dtype_code(v_cache))
+    _lib.check("think_append_kv", _lib.lib.think_append_kv(
+        ctypes.byref(dims), _p(k_new), _p(v_new), _p(seq_lens), _p(kept_idx), int(keep),
+        _p(k_thin), _p(v_cache), _stream(stream)))
+    return seq_lens

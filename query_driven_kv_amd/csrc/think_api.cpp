@@ -181,6 +181,19 @@ int think_decode_attn_combine(const think_dims* d, const int32_t* seq_lens, int3
                                                      (hipStream_t)stream));
 }
 
+int think_append_kv(const think_dims* d, const void* k_new, const void* v_new, int32_t* seq_lens,
+                    const int32_t* kept_idx, int32_t keep, void* k_thin, void* v_cache,
+                    void* stream) {
+    int st = check_dims(d);
+    if (st != THINK_OK) return st;
+    if (!k_new || !v_new || !seq_lens || !kept_idx || !k_thin || !v_cache) return THINK_ERR_NULL;
+    if (keep < 1 || keep > d->head_dim) return THINK_ERR_KEEP;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_thin) || !aligned16(v_cache))
+        return THINK_ERR_UNSUPPORTED;
+    return hip_status(thinkkv::launch_append(*d, k_new, v_new, seq_lens, kept_idx, keep, k_thin,
+                                             v_cache, (hipStream_t)stream));
+}
+
 const char* think_status_string(int status) {
     switch (status) {
         case THINK_OK: return "ok";

@@ -124,6 +124,9 @@ hipError_t launch_select(const think_dims& d, const float* scores, int keep, int
 hipError_t launch_compact(const think_dims& d, const CompactGeom& g, const void* k_cache,
                           const int32_t* seq_lens, const int32_t* kept_idx, int keep,
                           void* k_thin, hipStream_t s);
+hipError_t launch_append(const think_dims& d, const void* k_new, const void* v_new,
+                         int32_t* seq_lens, const int32_t* kept_idx, int keep, void* k_thin,
+                         void* v_cache, hipStream_t s);
 hipError_t launch_decode_partial(const think_dims& d, const DecodeGeom& g, const void* q,
                                  const void* k_thin, const void* v_cache, const int32_t* seq_lens,
                                  const int32_t* kept_idx, int keep, float scale, float* partials,

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_header_declarations_are_all_exported(L):
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     assert sorted(L.EXPORTS) == names
     so = ctypes.CDLL(L.LIB_PATH)
     for n in names:
@@ -42,7 +42,7 @@ def test_only_the_abi_is_exported(L):
 
 def test_version_and_keep_rounding(L):
     lib = L.lib
-    assert lib.think_abi_version() == 1
+    assert lib.think_abi_version() == 2
     assert [lib.think_keep_from_ratio(128, r) for r in (0.4, 0.6, 0.5)] == [77, 51, 64]
     assert lib.think_keep_from_ratio(16, 0.5) == 8
     assert lib.think_keep_from_ratio(128, 0.0) == 128
@@ -93,6 +93,26 @@ def test_score_rejects_bad_dims(L, kw, status):
     assert L.lib.think_compact_k(ctypes.byref(d), FAKE, FAKE, FAKE, 8, FAKE, None) == status
     assert L.lib.think_decode_attn(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 8, 0.1, FAKE,
                                    FAKE, 1 << 30, None) == status
+    assert L.lib.think_append_kv(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 8, FAKE, FAKE,
+                                 None) == status
+
+
+def test_append_validation(L):
+    lib = L.lib
+    d = dims(L)
+    assert lib.think_append_kv(None, FAKE, FAKE, FAKE, FAKE, 8, FAKE, FAKE, None) == -1
+    for i in range(6):                                   # each required pointer
+        args = [FAKE] * 6
+        args[i] = None
+        k_new, v_new, lens, idx, kt, vc = args
+        assert lib.think_append_kv(ctypes.byref(d), k_new, v_new, lens, idx, 8, kt, vc,
+                                   None) == -1
+    for keep in (0, 129):
+        assert lib.think_append_kv(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, keep, FAKE, FAKE,
+                                   None) == -3
+    odd = ctypes.c_void_p(0x100008)
+    assert lib.think_append_kv(ctypes.byref(d), odd, FAKE, FAKE, FAKE, 8, FAKE, FAKE, None) == -5
+    assert lib.think_append_kv(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 8, FAKE, odd, None) == -5
 
 
 def test_null_keep_window_workspace_and_alignment(L):

@@ -1,0 +1,66 @@
+"""GPU parity of the decode-time append against the oracle: think_append_kv
+then think_decode_attn, several steps in a row, on the same seeded inputs.
+The thin-key and value caches and the lengths must match the oracle's byte
+for byte after every step (the padding beyond the new length still holds the
+NaN sentinel), and the attention over len_b + 1 tokens must be within the
+decode tolerance.  Cases cover ragged batches, odd keep, fp32, a sequence that
+fills its last slot and one already at capacity (left as it is)."""
+import numpy as np
+import pytest
+import torch
+
+import kvsynth
+import oracle
+from gpu_util import row_rel_err, to_dev, to_host, tol_for
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # seed, lens, Hq, Hkv, D, S_cap, keep, dtype
+    (50, [300, 17, 511], 8, 2, 128, 512, 64, "bf16"),     # matrix-core decode, ragged
+    (51, [1000, 998], 4, 1, 128, 1000, 51, "bf16"),        # odd keep; one sequence full
+    (52, [63, 40], 6, 3, 64, 66, 20, "f32"),               # general decode, fp32
+    (53, [5, 2047], 32, 8, 128, 2048, 77, "bf16"),         # slot S_cap-1 filled by the first step
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"append{c[0]}" for c in CASES])
+def test_append_then_decode(case):
+    import query_driven_kv_amd as qdk
+    seed, lens, Hq, Hkv, D, S, keep, dtype = case
+    B = len(lens)
+    print(f"[append] seed {seed}: B={B} S={S} Hq={Hq} Hkv={Hkv} D={D} keep={keep} {dtype}",
+          flush=True)
+    cfg = kvsynth.custom(f"append{seed}", batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D,
+                         seq_capacity=S, obs_window=4, keep=keep, dtype=dtype, cfg_id=91,
+                         lowrank=8 if D >= 64 else 0)
+    L = kvsynth.make_layer(cfg, layer=seed)
+    lens = np.asarray(lens, np.int32)
+    nan = kvsynth.nan_value(dtype)
+    for b in range(B):
+        L["k_cache"][b, lens[b]:] = nan
+        L["v_cache"][b, lens[b]:] = nan
+    s = oracle.score(L["k_cache"], lens, L["q_obs"])
+    idx, _ = oracle.select(s, keep)
+    thin = oracle.compact(L["k_cache"], lens, idx, fill=nan)
+    v = L["v_cache"]
+    scale = np.float32(1.0 / np.sqrt(D))
+
+    thin_d, v_d, lens_d, idx_d = to_dev(thin), to_dev(v), to_dev(lens), to_dev(idx)
+    o_thin, o_v, o_lens = thin, v, lens
+    for step in range(3):
+        k_new, v_new = kvsynth.decode_kv(cfg, seed, step, L["channel_scale"])
+        q = kvsynth.decode_q(cfg, seed, step, L["channel_scale"])
+        qdk.think_append_kv(to_dev(k_new), to_dev(v_new), lens_d, idx_d, thin_d, v_d)
+        out = qdk.think_decode_attn(to_dev(q), thin_d, v_d, lens_d, idx_d, scale)
+        torch.cuda.synchronize()
+        o_thin, o_v, o_lens = oracle.append(k_new, v_new, o_lens, idx, o_thin, o_v)
+        np.testing.assert_array_equal(to_host(lens_d), o_lens)
+        np.testing.assert_array_equal(to_host(thin_d).view(np.uint8), o_thin.view(np.uint8))
+        np.testing.assert_array_equal(to_host(v_d).view(np.uint8), o_v.view(np.uint8))
+        ref = oracle.decode(q, o_thin, o_v, o_lens, idx, scale)
+        err = row_rel_err(out, ref)
+        assert err.max() <= tol_for(dtype), f"step {step}: decode row error {err.max():.3e}"
+        print(f"[append] seed {seed} step {step}: lens {o_lens.tolist()}, "
+              f"decode row err {err.max():.2e}", flush=True)
+    assert (o_lens == np.minimum(lens + 3, S)).all()
