@@ -96,6 +96,27 @@ class Workload:
                 del L
         self.host0 = host0
         self.lens_host = host0["seq_lens"]
+        # Cold protocol: a workload smaller than 1 GiB in all is replicated so
+        # that successive calls rotate over copies and read from HBM rather
+        # than from the 256 MB last-level cache.
+        e = 2 if cfg.dtype == "bf16" else 4
+        per_layer = B * S * Hkv * (2 * D + keep) * e
+        self.ncopies = 1 if cfg.layers * per_layer >= (1 << 30) else -(-(1 << 30) // (cfg.layers * per_layer))
+        self.sets = [self.layers]
+        for _ in range(self.ncopies - 1):
+            cp = []
+            for ent in self.layers:
+                c = {k: ent[k].clone() for k in ("k", "v", "qo", "lens", "q")}
+                c["scores"] = torch.empty_like(ent["scores"])
+                c["idx"] = torch.empty_like(ent["idx"])
+                c["tie"] = torch.empty_like(ent["tie"])
+                c["thin"] = torch.empty_like(ent["thin"])
+                cp.append(c)
+            self.sets.append(cp)
+        if self.ncopies > 1:
+            log(f"{self.ncopies} copies of the inputs rotate between calls (cold protocol)")
+        self.sc_i = 0
+        self.dc_i = 0
         self.out = torch.empty(B, Hq, D, dtype=tdt, device=dev)
         code = qdk.THINK_BF16 if cfg.dtype == "bf16" else qdk.THINK_F32
         self.dims = qdk.make_dims(B, Hq, Hkv, D, S, code)
@@ -113,7 +134,9 @@ class Workload:
         d, keep = ctypes.byref(self.dims), self.cfg.keep
         W = self.cfg.obs_window
         ws, wsn = P(self.ws_s.data_ptr()), self.ws_s.numel()
-        for e in self.layers:
+        layers = self.sets[self.sc_i % self.ncopies]
+        self.sc_i += 1
+        for e in layers:
             _lib.check("think_score_select", lib.think_score_select(
                 d, P(e["k"].data_ptr()), P(e["lens"].data_ptr()), P(e["qo"].data_ptr()), W, keep,
                 P(e["scores"].data_ptr()), P(e["idx"].data_ptr()), P(e["tie"].data_ptr()), ws, wsn,
@@ -124,15 +147,28 @@ class Workload:
 
     def prepare_decode(self):
         P = ctypes.c_void_p
+        # dec_args[copy][step][layer]; successive calls take successive copies
         self.dec_args = []
         qstep = self.cfg.batch * self.cfg.n_q_heads * self.cfg.head_dim
         esz = self.out.element_size()
-        for s in range(self.cfg.decode_steps):
-            row = []
-            for e in self.layers:
-                row.append((P(e["q"].data_ptr() + s * qstep * esz), P(e["thin"].data_ptr()),
-                            P(e["v"].data_ptr()), P(e["lens"].data_ptr()), P(e["idx"].data_ptr())))
-            self.dec_args.append(row)
+        for layers in self.sets:
+            steps = []
+            for s in range(self.cfg.decode_steps):
+                row = []
+                for e in layers:
+                    row.append((P(e["q"].data_ptr() + s * qstep * esz), P(e["thin"].data_ptr()),
+                                P(e["v"].data_ptr()), P(e["lens"].data_ptr()),
+                                P(e["idx"].data_ptr())))
+                steps.append(row)
+            self.dec_args.append(steps)
+
+    def decode_calls(self, steps=None):
+        """The decode calls of one step, in order, rotating over the copies."""
+        for s in range(self.cfg.decode_steps if steps is None else steps):
+            for l in range(self.cfg.layers):
+                c = self.dc_i % self.ncopies
+                self.dc_i += 1
+                yield self.dec_args[c][s][l]
 
     def decode_kernel_times(self, stream, torch):
         """One step's decode calls in split-phase form, with HIP events on the
@@ -142,19 +178,18 @@ class Workload:
         lib, P = _lib.lib, ctypes.c_void_p
         d, keep = ctypes.byref(self.dims), self.cfg.keep
         out, ws, wsn = P(self.out.data_ptr()), P(self.ws_d.data_ptr()), self.ws_d.numel()
-        n = sum(len(r) for r in self.dec_args)
+        n = self.cfg.decode_steps * self.cfg.layers
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(n)]
         k = 0
-        for row in self.dec_args:
-            for (q, thin, v, lens, idx) in row:
-                ev[k][0].record()
-                _lib.check("think_decode_attn_partial", lib.think_decode_attn_partial(
-                    d, q, thin, v, lens, idx, keep, self.scale, ws, wsn, stream))
-                ev[k][1].record()
-                _lib.check("think_decode_attn_combine", lib.think_decode_attn_combine(
-                    d, lens, keep, out, ws, wsn, stream))
-                k += 1
+        for (q, thin, v, lens, idx) in self.decode_calls():
+            ev[k][0].record()
+            _lib.check("think_decode_attn_partial", lib.think_decode_attn_partial(
+                d, q, thin, v, lens, idx, keep, self.scale, ws, wsn, stream))
+            ev[k][1].record()
+            _lib.check("think_decode_attn_combine", lib.think_decode_attn_combine(
+                d, lens, keep, out, ws, wsn, stream))
+            k += 1
         torch.cuda.synchronize()
         return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3, n
 
@@ -164,11 +199,10 @@ class Workload:
         d, keep = ctypes.byref(self.dims), self.cfg.keep
         out, ws, wsn = P(self.out.data_ptr()), P(self.ws_d.data_ptr()), self.ws_d.numel()
         fn = lib.think_decode_attn
-        for row in self.dec_args[:steps]:
-            for (q, thin, v, lens, idx) in row:
-                rc = fn(d, q, thin, v, lens, idx, keep, self.scale, out, ws, wsn, stream)
-                if rc:
-                    _lib.check("think_decode_attn", rc)
+        for (q, thin, v, lens, idx) in self.decode_calls(steps):
+            rc = fn(d, q, thin, v, lens, idx, keep, self.scale, out, ws, wsn, stream)
+            if rc:
+                _lib.check("think_decode_attn", rc)
 
     # ---- algorithmic bytes
     def bytes_model(self):
@@ -183,6 +217,40 @@ class Workload:
         dec_call = Kt + K + 2 * q          # |K_thin| + |V| + |q| + |out|  (|V| == |K|)
         return dict(tokens=tok, sc_layer=sc_layer, dec_call=dec_call,
                     sc_min_layer=K + Kt + Qw)
+
+
+def append_time(cfg, torch, qdk, dev, calls=512):
+    """Mean duration of one decode-time append (think_append_kv) of this
+    workload's batch and head shape, over `calls` appends into fresh rows of a
+    scratch cache (the bench's own caches are full and stay untouched).
+    Returns (microseconds per call, bytes per call)."""
+    from query_driven_kv_amd import _lib
+    P = ctypes.c_void_p
+    B, Hkv, D, keep = cfg.batch, cfg.n_kv_heads, cfg.head_dim, cfg.keep
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    S = calls + 1
+    thin = torch.zeros(B, S, Hkv, keep, dtype=tdt, device=dev)
+    v = torch.zeros(B, S, Hkv, D, dtype=tdt, device=dev)
+    kn = torch.randn(B, Hkv, D, device=dev).to(tdt)
+    vn = torch.randn(B, Hkv, D, device=dev).to(tdt)
+    idx = torch.arange(keep, dtype=torch.int32, device=dev).repeat(B, Hkv, 1).contiguous()
+    lens = torch.zeros(B, dtype=torch.int32, device=dev)
+    dims = qdk.make_dims(B, cfg.n_q_heads, Hkv, D, S, tdt)
+    sp = P(torch.cuda.current_stream().cuda_stream)
+    args = (ctypes.byref(dims), P(kn.data_ptr()), P(vn.data_ptr()), P(lens.data_ptr()),
+            P(idx.data_ptr()), keep, P(thin.data_ptr()), P(v.data_ptr()), sp)
+    fn = _lib.lib.think_append_kv
+    _lib.check("think_append_kv", fn(*args))
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(calls - 1):
+        fn(*args)
+    e1.record()
+    torch.cuda.synchronize()
+    assert int(lens.min().item()) == calls, "append did not advance every sequence"
+    e = thin.element_size()
+    return e0.elapsed_time(e1) * 1e3 / (calls - 1), B * Hkv * (2 * D + keep + D) * e
 
 
 def decode_source_hash():
@@ -281,8 +349,9 @@ def main():
     bm = wl.bytes_model()
     n_dec = cfg.decode_steps * cfg.layers
 
-    for _ in range(args.warmup):
-        wl.score_compact(sp)
+    for _ in range(max(args.warmup, 1 if wl.ncopies > 1 else 0)):
+        for _ in range(wl.ncopies):              # every copy's thin cache is filled
+            wl.score_compact(sp)
         wl.decode(sp)
     torch.cuda.synchronize()
     log("warmup done")
@@ -322,6 +391,8 @@ def main():
         part_us, n_part = wl.decode_kernel_times(sp, torch)
         log(f"chunk-pass kernel: {part_us:.2f} us mean over {n_part} launches")
     achieved = bm["dec_call"] / (part_us * 1e-6) / 1e9 if n_part else None
+    app_us, app_bytes = append_time(cfg, torch, qdk, dev)
+    log(f"decode-time append: {app_us:.2f} us per call")
     traffic, traffic_src = committed_traffic(cfg.name)
 
     result = {
@@ -355,6 +426,9 @@ def main():
                        "us_per_call": round(dec_call_us, 2),
                        "kv_tokens_per_s": float(f"{tok * n_dec / (dec_ms / 1e3):.4g}"),
                        "bytes_per_call": bm["dec_call"]},
+            "append": {"us_per_call": round(app_us, 2), "bytes_per_call": app_bytes,
+                       "note": "think_append_kv, timed apart from the step (the workload's "
+                               "caches are full)"},
         },
         "roofline": {"kernel": "k_decode_mfma (think_decode_attn chunk pass)",
                      "bound": "hbm", "achieved": round(achieved, 1) if achieved else None,
@@ -367,6 +441,7 @@ def main():
                                 f"chunk-pass launches of one step, after the timed steps"),
                      "traffic_source": traffic_src},
         "near_ties": near,
+        "input_copies": wl.ncopies,
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
