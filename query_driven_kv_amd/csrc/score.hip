@@ -112,86 +112,107 @@ __global__ __launch_bounds__(1024) void k_score_finalize(
     const int kv = blockIdx.x, b = blockIdx.y;
     const int tid = threadIdx.x, nth = blockDim.x;
     const int G = Hq / Hkv, R = Hkv * D, Q = D / 4, SG = nth / Q;
-    const int len = clamp_len(seq_lens, b, s_cap);
-    const int ns = (len + tpw - 1) / tpw;
-
     __shared__ double red[4096];                 // [SG][D] split-group sums, then [RG][G*D]
     __shared__ double qn[4096];                  // [g][c] sqrt(Q2)  (G * D <= 4096)
-    __shared__ float s_sc[256];
+    __shared__ __align__(16) float s_sc[256];
     __shared__ int s_scratch[1024];
     __shared__ float s_cut[2];
 
+    // The first round of loads is issued before any is waited on: the length
+    // (a vector load, so waiting for it leaves the rest in flight), this
+    // thread's first eight split partials and its first eight window rows.
+    // Their indices are clamped into range instead of branched on, and the
+    // slots past the length's split count or past the row group are dropped
+    // when summed (a dropped slot adds +0.0, so the sums are those of the
+    // plain loops).
+    const int len_v = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(seq_lens + b, 4u), 0, 0, 0);
+    const int cq = tid % Q, sg = tid / Q;
+    const float4* p = reinterpret_cast<const float4*>(partials + (size_t)b * nsplit * R +
+                                                      (size_t)kv * D) + cq;
+    const size_t sstride = (size_t)R / 4;
+    float4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = p[(size_t)min(sg + k * SG, nsplit - 1) * sstride];
+
+    const int GD = G * D, nv = GD / EPV;         // 16-byte vectors per window row
+    int RG = nth / nv;
+    if (RG > 4096 / GD) RG = 4096 / GD;
+    if (RG > W) RG = W;
+    if (RG < 1) RG = 1;
+    const int qv = tid % nv, rg = tid / nv;
+    const bool qact = rg < RG;
+    const int i0 = qact ? rg * W / RG : 0, i1 = qact ? (rg + 1) * W / RG : 0;
+    const uint4* qb = reinterpret_cast<const uint4*>(
+        q_obs + ((size_t)b * W * Hq + (size_t)kv * G) * D) + qv;
+    const size_t rstride = (size_t)Hq * D / EPV;     // vectors between window rows
+    uint4 x[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = qb[(size_t)min(i0 + k, W - 1) * rstride];
+
+    const int len_raw = __builtin_amdgcn_readfirstlane(len_v);
+    const int len = len_raw < 0 ? 0 : (len_raw > s_cap ? s_cap : len_raw);
+    const int ns = (len + tpw - 1) / tpw;
+
     {
-        const int cq = tid % Q, sg = tid / Q;
-        const float4* p = reinterpret_cast<const float4*>(partials + (size_t)b * nsplit * R +
-                                                          (size_t)kv * D) + cq;
-        const size_t sstride = (size_t)R / 4;
         double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
-        for (int s0 = sg; s0 < ns; s0 += 8 * SG) {
-            float4 v[8];
+        auto add = [&](const float4 (&w)[8], int s0) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                const int sp = s0 + k * SG;
-                v[k] = sp < ns ? p[(size_t)sp * sstride] : make_float4(0.f, 0.f, 0.f, 0.f);
+                const bool ok = s0 + k * SG < ns;
+                a0 += ok ? (double)w[k].x : 0.0;
+                a1 += ok ? (double)w[k].y : 0.0;
+                a2 += ok ? (double)w[k].z : 0.0;
+                a3 += ok ? (double)w[k].w : 0.0;
             }
+        };
+        if (sg < ns) add(v, sg);
+        for (int s0 = sg + 8 * SG; s0 < ns; s0 += 8 * SG) {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                a0 += (double)v[k].x;
-                a1 += (double)v[k].y;
-                a2 += (double)v[k].z;
-                a3 += (double)v[k].w;
-            }
+            for (int k = 0; k < 8; ++k) v[k] = p[(size_t)min(s0 + k * SG, nsplit - 1) * sstride];
+            add(v, s0);
         }
         red[sg * D + 4 * cq + 0] = a0;
         red[sg * D + 4 * cq + 1] = a1;
         red[sg * D + 4 * cq + 2] = a2;
         red[sg * D + 4 * cq + 3] = a3;
     }
+    // window-query squares of this thread's vector over its rows, in row order
+    double acc[EPV];
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) acc[e] = 0.0;
+    auto addq = [&](const uint4 (&w)[8], int r0) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            float f[EPV];
+            unpack(w[k], f, E{});
+            const bool ok = r0 + k < i1;
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) acc[e] += ok ? (double)f[e] * (double)f[e] : 0.0;
+        }
+    };
+    if (i0 < i1) addq(x, i0);
+    for (int i = i0 + 8; i < i1; i += 8) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[k] = qb[(size_t)min(i + k, W - 1) * rstride];
+        addq(x, i);
+    }
+
     __syncthreads();
     double K2 = 0.0;
     if (tid < D)
         for (int r = 0; r < SG; ++r) K2 += red[r * D + tid];
     __syncthreads();                             // red is reused below
-
-    {
-        const int GD = G * D, nv = GD / EPV;     // 16-byte vectors per window row
-        int RG = nth / nv;
-        if (RG > 4096 / GD) RG = 4096 / GD;
-        if (RG > W) RG = W;
-        if (RG < 1) RG = 1;
-        const int v = tid % nv, rg = tid / nv;
-        if (rg < RG) {
-            const uint4* qb = reinterpret_cast<const uint4*>(
-                q_obs + ((size_t)b * W * Hq + (size_t)kv * G) * D) + v;
-            const size_t rstride = (size_t)Hq * D / EPV;   // vectors between window rows
-            const int i0 = rg * W / RG, i1 = (rg + 1) * W / RG;
-            double acc[EPV];
+    if (qact) {
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) acc[e] = 0.0;
-            for (int i = i0; i < i1; i += 8) {
-                uint4 x[8];
-#pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    x[k] = i + k < i1 ? qb[(size_t)(i + k) * rstride] : make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    float f[EPV];
-                    unpack(x[k], f, E{});
-#pragma unroll
-                    for (int e = 0; e < EPV; ++e) acc[e] += (double)f[e] * (double)f[e];
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) red[rg * GD + v * EPV + e] = acc[e];
-        }
-        __syncthreads();
-        for (int pr = tid; pr < GD; pr += nth) {
-            double t = 0.0;
-            for (int r = 0; r < RG; ++r) t += red[r * GD + pr];
-            qn[pr] = sqrt(t);                    // index g*D + c
-        }
-        __syncthreads();
+        for (int e = 0; e < EPV; ++e) red[rg * GD + qv * EPV + e] = acc[e];
     }
+    __syncthreads();
+    for (int pr = tid; pr < GD; pr += nth) {
+        double t = 0.0;
+        for (int r = 0; r < RG; ++r) t += red[r * GD + pr];
+        qn[pr] = sqrt(t);                        // index g*D + c
+    }
+    __syncthreads();
 
     if (tid < D) {
         double qsum = 0.0;

@@ -15,7 +15,7 @@ __global__ __launch_bounds__(256) void k_select(const float* __restrict__ scores
                                                 int32_t* __restrict__ kept_idx,
                                                 int32_t* __restrict__ near_tie) {
     const int kv = blockIdx.x, b = blockIdx.y, Hkv = gridDim.x;
-    __shared__ float s[256];
+    __shared__ __align__(16) float s[256];
     __shared__ int scratch[256];
     __shared__ float cut[2];
     const size_t row = (size_t)b * Hkv + kv;

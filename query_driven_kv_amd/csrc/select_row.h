@@ -12,18 +12,21 @@
 namespace thinkkv {
 
 // Called by every thread of the workgroup (blockDim.x a multiple of 64 and
-// >= D); s[0..D) holds the scores in LDS.  scratch (>= blockDim.x ints) and
-// cut (2 floats) are LDS scratch.  The rank of each channel under the total
-// order is the number of channels ahead of it; the count is split over
-// blockDim/D thread groups and their partial counts added in a fixed order.
-// Ranks form a permutation, so no sort is needed; the output slot of a kept
-// channel (ascending order) comes from wave ballots and prefix popcounts.
+// >= D); s[0..D) holds the scores in LDS, 16-byte aligned.  scratch
+// (>= blockDim.x ints) and cut (2 floats) are LDS scratch.  The rank of each
+// channel under the total order is the number of channels ahead of it; the
+// count is split over up to 16 thread groups of whole 4-channel blocks (read
+// as one 16-byte LDS load each, so the reads pipeline) and their partial
+// counts are added in a fixed order.  Ranks form a permutation, so no sort is
+// needed; the output slot of a kept channel (ascending order) comes from wave
+// ballots and prefix popcounts.
 __device__ __forceinline__ void select_row(const float* s, int D, int keep, int* scratch,
                                            float* cut, int32_t* __restrict__ idx_out,
                                            int32_t* __restrict__ tie_out) {
     const int tid = threadIdx.x, nth = blockDim.x;
     int parts = nth / D;
     if (parts > 16) parts = 16;
+    while (parts > 1 && D % (4 * parts) != 0) --parts;   // D is a multiple of 8
     const int c = tid % D, part = tid / D;
     __shared__ int wave_kept[16];
     if (tid == 0) {
@@ -32,11 +35,15 @@ __device__ __forceinline__ void select_row(const float* s, int D, int keep, int*
     }
     if (part < parts) {
         const float x = s[c];
-        const int o0 = part * D / parts, o1 = (part + 1) * D / parts;
+        const int o0 = part * (D / parts), o1 = o0 + D / parts;
         int cnt = 0;
-        for (int o = o0; o < o1; ++o) {
-            const float y = s[o];
-            cnt += (y > x) | ((y == x) & (o < c));
+#pragma unroll 4
+        for (int o = o0; o < o1; o += 4) {
+            const float4 y = *reinterpret_cast<const float4*>(s + o);
+            cnt += (y.x > x) | ((y.x == x) & (o < c));
+            cnt += (y.y > x) | ((y.y == x) & (o + 1 < c));
+            cnt += (y.z > x) | ((y.z == x) & (o + 2 < c));
+            cnt += (y.w > x) | ((y.w == x) & (o + 3 < c));
         }
         scratch[part * D + c] = cnt;
     }
