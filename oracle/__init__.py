@@ -49,6 +49,8 @@ def _load():
     lib.oracle_compact.argtypes = [i32] * 5 + [vp, vp, vp, i32, vp]
     lib.oracle_decode.argtypes = [i32] * 6 + [vp, vp, vp, vp, vp, i32, dbl, vp]
     lib.oracle_append.argtypes = [i32] * 5 + [vp, vp, vp, vp, i32, vp, vp]
+    lib.oracle_prefill_write.argtypes = [i32] * 5 + [vp, vp, i32, i32, vp, vp, vp, vp]
+    lib.oracle_score_from_k2.argtypes = [i32] * 5 + [vp, vp, i32, vp]
     lib.oracle_full_attn.argtypes = [i32] * 6 + [vp, vp, vp, vp, dbl, vp]
     lib.oracle_residual_materialised.argtypes = [i32, i32, i32, vp, vp, vp]
     lib.oracle_residual_materialised.restype = dbl
@@ -151,6 +153,38 @@ def compact(k_cache, seq_lens, kept_idx, fill=None):
         out[...] = fill
     _check(_load().oracle_compact(B, S, Hkv, D, _dtype_code(k_cache), _ptr(k_cache), _ptr(lens),
                                   _ptr(idx), keep, _ptr(out)), "compact")
+    return out
+
+
+def prefill_write(k_rows, v_rows, t0, seq_lens, k_cache, v_cache, k2):
+    """Prefill-fused scoring, write half: rows t of the chunk go to positions
+    t0+t < len_b of the caches and their squares are added to K2 (fp64
+    [B,Hkv,D]).  Returns new copies (k_cache, v_cache, k2)."""
+    k_rows, v_rows = _c(k_rows), _c(v_rows)
+    kc, vc = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
+    acc = np.array(k2, dtype=np.float64, copy=True)
+    lens = _c(seq_lens, np.int32)
+    B, S, Hkv, D = kc.shape
+    n = k_rows.shape[1]
+    if (k_rows.shape != (B, n, Hkv, D) or v_rows.shape != (B, n, Hkv, D) or acc.shape != (B, Hkv, D)
+            or len({k_rows.dtype, v_rows.dtype, kc.dtype, vc.dtype}) != 1):
+        raise ValueError("shape or dtype mismatch")
+    _check(_load().oracle_prefill_write(B, S, Hkv, D, _dtype_code(kc), _ptr(k_rows), _ptr(v_rows),
+                                        int(t0), n, _ptr(lens), _ptr(kc), _ptr(vc), _ptr(acc)),
+           "prefill_write")
+    return kc, vc, acc
+
+
+def score_from_k2(k2, q_obs):
+    """Stage (a) from gathered sums: sqrt(K2) * sum_g sqrt(sum_i Q_w^2); fp64 [B,Hkv,D]."""
+    k2, q_obs = _c(k2, np.float64), _c(q_obs)
+    B, Hkv, D = k2.shape
+    Bq, W, Hq, Dq = q_obs.shape
+    if (Bq, Dq) != (B, D) or Hq % Hkv:
+        raise ValueError("shape mismatch")
+    out = np.empty((B, Hkv, D), np.float64)
+    _check(_load().oracle_score_from_k2(B, Hq, Hkv, D, _dtype_code(q_obs), _ptr(k2), _ptr(q_obs),
+                                        W, _ptr(out)), "score_from_k2")
     return out
 
 

@@ -129,6 +129,76 @@ int oracle_score(int B, int S_cap, int Hq, int Hkv, int D, int dtype,
     return bad ? -2 : 0;
 }
 
+/* ---------------------------------------------------------------------------
+ * Prefill-fused scoring (the step before the path).  Stage (a) needs the
+ * keys only through K2[b,kv,c] = sum_t K[b,t,kv,c]^2, so the sums can be
+ * gathered while the prompt's keys are written to the cache, chunk by chunk,
+ * and the score later needs no key read.
+ *
+ * Write: a chunk of n_rows new rows per sequence at positions t0 .. t0+n_rows-1:
+ *   K[b,t0+t,kv,:] = k_rows[b,t,kv,:],  V[b,t0+t,kv,:] = v_rows[b,t,kv,:]
+ *   K2[b,kv,c]   += k_rows[b,t,kv,c]^2
+ * for every t with t0+t < min(len_b, S_cap) (seq_lens = the prompts' lengths);
+ * other rows are neither written nor counted.  Rows in ascending t.
+ * Layouts: k_rows, v_rows [B,n_rows,Hkv,D]; K2 fp64 [B,Hkv,D].
+ * ------------------------------------------------------------------------- */
+int oracle_prefill_write(int B, int S_cap, int Hkv, int D, int dtype, const void *k_rows,
+                         const void *v_rows, int t0, int n_rows, const int32_t *seq_lens,
+                         void *k_cache, void *v_cache, double *k2) {
+    if (!dims_ok(B, S_cap, Hkv, Hkv, D, dtype) || t0 < 0 || n_rows < 0) return -1;
+    if (!k_rows || !v_rows || !seq_lens || !k_cache || !v_cache || !k2) return -1;
+    if (!lens_ok(B, S_cap, seq_lens)) return -1;
+    const size_t es = elem_size(dtype), row = (size_t)Hkv * D;
+    int bad = 0;
+    for (int b = 0; b < B; ++b) {
+        for (int t = 0; t < n_rows; ++t) {
+            const int pos = t0 + t;
+            if (pos >= seq_lens[b]) break;
+            const size_t src = ((size_t)b * n_rows + t) * row;
+            const size_t dst = ((size_t)b * S_cap + pos) * row;
+            memcpy((unsigned char *)k_cache + dst * es, (const unsigned char *)k_rows + src * es,
+                   row * es);
+            memcpy((unsigned char *)v_cache + dst * es, (const unsigned char *)v_rows + src * es,
+                   row * es);
+            for (size_t i = 0; i < row; ++i) {
+                const double x = widen(k_rows, dtype, src + i);
+                if (!isfinite(x)) bad = 1;
+                k2[(size_t)b * row + i] += x * x;
+            }
+        }
+    }
+    return bad ? -2 : 0;
+}
+
+/* Score from the gathered sums: s[b,kv,c] = sqrt(K2[b,kv,c]) *
+ * sum_g sqrt(sum_i Q_w[b,i,kv*G+g,c]^2), the stage (a) formula with K2 given. */
+int oracle_score_from_k2(int B, int Hq, int Hkv, int D, int dtype, const double *k2,
+                         const void *q_obs, int W, double *scores) {
+    if (!dims_ok(B, 1, Hq, Hkv, D, dtype) || W < 1) return -1;
+    if (!k2 || !q_obs || !scores) return -1;
+    const int G = Hq / Hkv;
+    int bad = 0;
+    for (int b = 0; b < B; ++b)
+        for (int kv = 0; kv < Hkv; ++kv)
+            for (int c = 0; c < D; ++c) {
+                const double K2 = k2[((size_t)b * Hkv + kv) * D + c];
+                if (!isfinite(K2) || K2 < 0.0) bad = 1;
+                double qsum = 0.0;
+                for (int g = 0; g < G; ++g) {
+                    double Q2 = 0.0;
+                    for (int i = 0; i < W; ++i) {
+                        const double q =
+                            widen(q_obs, dtype, (((size_t)b * W + i) * Hq + kv * G + g) * D + c);
+                        if (!isfinite(q)) bad = 1;
+                        Q2 += q * q;
+                    }
+                    qsum += sqrt(Q2);
+                }
+                scores[((size_t)b * Hkv + kv) * D + c] = sqrt(K2) * qsum;
+            }
+    return bad ? -2 : 0;
+}
+
 /* The other reading of the grouped-query aggregation, kept for reports only:
  * the Frobenius norm of the stacked (G*W) x len block, i.e.
  * sqrt(K2) * sqrt(sum_g Q2[g]).  Not used by the pruning path. */

@@ -475,3 +475,45 @@ def test_decode_after_append_attends_to_the_new_token():
     o = oracle.decode(q, kt, vc, lens2, idx, 1.0)
     np.testing.assert_array_equal(o[0, 0], v_new[0, 0].astype(np.float64))
     np.testing.assert_array_equal(o[0, 1], v_new[0, 0].astype(np.float64))
+
+
+# --------------------------------------------------------------------------- prefill-fused scoring
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_write_places_rows_and_gathers_squares(dtype):
+    """Writing a prompt's keys chunk by chunk puts every row t < len_b at its
+    position, writes nothing past len_b, and gathers exactly the per-channel
+    sums of squares that a library sum over the finished cache gives."""
+    cfg, L = _case(31, B=3, Hq=4, Hkv=2, D=16, S=40, dtype=dtype, lens=[40, 23, 1])
+    src_k, src_v, lens = L["k_cache"], L["v_cache"], L["seq_lens"]
+    nan = kvsynth.nan_value(dtype)
+    kc = np.full_like(src_k, nan)
+    vc = np.full_like(src_v, nan)
+    k2 = np.zeros((3, 2, 16))
+    t0 = 0
+    for n in (7, 1, 13, 9, 10):                          # chunks of uneven sizes, 40 rows in all
+        kc, vc, k2 = oracle.prefill_write(src_k[:, t0:t0 + n], src_v[:, t0:t0 + n], t0, lens,
+                                          kc, vc, k2)
+        t0 += n
+    for b, m in enumerate(lens):
+        np.testing.assert_array_equal(kc[b, :m].view(np.uint8), src_k[b, :m].view(np.uint8))
+        np.testing.assert_array_equal(vc[b, :m].view(np.uint8), src_v[b, :m].view(np.uint8))
+        assert np.isnan(kvsynth.as_float(kc[b, m:])).all() and np.isnan(kvsynth.as_float(vc[b, m:])).all()
+        ref = np.square(kvsynth.as_float(src_k[b, :m]).astype(np.float64)).sum(axis=0)
+        np.testing.assert_allclose(k2[b], ref, rtol=1e-14, atol=0)
+
+
+def test_score_from_gathered_sums_matches_the_definition():
+    """The score from the gathered sums equals the materialised definition of
+    stage (a) on the finished cache, and so equals the score read off the
+    cache itself."""
+    cfg, L = _case(32, B=2, Hq=6, Hkv=2, D=12, S=30, W=5, lens=[30, 17], lowrank=4)
+    lens = L["seq_lens"]
+    kc = np.zeros_like(L["k_cache"])
+    vc = np.zeros_like(L["v_cache"])
+    k2 = np.zeros((2, 2, 12))
+    for t0 in range(0, 30, 8):
+        kc, vc, k2 = oracle.prefill_write(L["k_cache"][:, t0:t0 + 8], L["v_cache"][:, t0:t0 + 8],
+                                          t0, lens, kc, vc, k2)
+    s = oracle.score_from_k2(k2, L["q_obs"])
+    ref = _def_scores(L["k_cache"], lens, L["q_obs"], cfg.group)
+    np.testing.assert_allclose(s, ref, rtol=1e-12, atol=0)
