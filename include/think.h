@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define THINK_ABI_VERSION 2
+#define THINK_ABI_VERSION 3
 
 #ifndef THINK_API
 #define THINK_API __attribute__((visibility("default")))
@@ -207,6 +207,39 @@ THINK_API int think_decode_attn_combine(const think_dims *d, const int32_t *seq_
 THINK_API int think_append_kv(const think_dims *d, const void *k_new, const void *v_new,
                               int32_t *seq_lens, const int32_t *kept_idx, int32_t keep,
                               void *k_thin, void *v_cache, void *stream);
+
+/*
+ * Prefill-fused scoring, the step before stage (a).  Stage (a) reads the keys
+ * only through K2[b,kv,c] = sum_{t<len_b} K[b,t,kv,c]^2, and the prompt's keys
+ * pass through the cache write anyway, so the sums can be gathered there and
+ * the score computed later without reading the key cache.
+ *
+ * think_prefill_write_kv writes one chunk of a prompt: for t < n_rows with
+ * t0 + t < min(len_b, S_cap) (seq_lens = the prompts' lengths),
+ *   k_cache[b,t0+t,:,:] = k_rows[b,t,:,:],  v_cache[b,t0+t,:,:] = v_rows[b,t,:,:]
+ * and adds the squares of those key rows to k2_state.  Other rows are neither
+ * written nor counted.
+ *   k_rows, v_rows    [B,n_rows,Hkv,D] dtype, n_rows >= 0, t0 >= 0
+ *   k2_state          >= think_k2_state_bytes(d), 16-byte aligned, caller-owned,
+ *                     zero-filled before a prompt's first chunk; every call adds
+ *                     its chunk (fixed-order fp64 sums, no atomics).  Calls that
+ *                     share a state must be ordered (same stream).
+ * think_score_select_k2 computes the scores of think_score from the state (no
+ * key read) and, when kept_idx is not NULL, the selection of think_select:
+ *   scores    out, fp32 [B,Hkv,D] or NULL (then kept_idx is required)
+ *   kept_idx  out, int32 [B,Hkv,keep] or NULL;  near_tie as for think_select
+ * After a prompt is written completely, the scores equal think_score on the
+ * written cache up to rounding (each within 1e-6 relative of exact).
+ */
+THINK_API size_t think_k2_state_bytes(const think_dims *d);
+THINK_API int think_prefill_write_kv(const think_dims *d, const void *k_rows, const void *v_rows,
+                                     int32_t t0, int32_t n_rows, const int32_t *seq_lens,
+                                     void *k_cache, void *v_cache, void *k2_state,
+                                     size_t k2_state_bytes, void *stream);
+THINK_API int think_score_select_k2(const think_dims *d, const void *k2_state,
+                                    size_t k2_state_bytes, const void *q_obs, int32_t obs_window,
+                                    int32_t keep, float *scores, int32_t *kept_idx,
+                                    int32_t *near_tie, void *stream);
 
 /* Static description of a status code. */
 THINK_API const char *think_status_string(int status);

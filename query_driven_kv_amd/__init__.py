@@ -20,6 +20,7 @@ from ._lib import THINK_BF16, THINK_F32, ThinkError, think_dims
 __all__ = ["think_score", "think_score_select", "think_select", "think_compact_k",
            "think_decode_attn",
            "think_decode_attn_partial", "think_decode_attn_combine", "think_append_kv",
+           "think_k2_state_bytes", "think_prefill_write_kv", "think_score_select_k2",
            "think_keep_from_ratio", "think_score_workspace_bytes", "think_decode_workspace_bytes",
            "think_abi_version", "make_dims", "ThinkError", "think_dims", "LIB_PATH"]
 
@@ -243,3 +244,51 @@ def think_append_kv(k_new, v_new, seq_lens, kept_idx, k_thin, v_cache, *, stream
         ctypes.byref(dims), _p(k_new), _p(v_new), _p(seq_lens), _p(kept_idx), int(keep),
         _p(k_thin), _p(v_cache), _stream(stream)))
     return seq_lens
+
+
+def think_k2_state_bytes(dims):
+    return int(_lib.lib.think_k2_state_bytes(ctypes.byref(dims)))
+
+
+def think_prefill_write_kv(k_rows, v_rows, t0, seq_lens, k_cache, v_cache, k2_state, *,
+                           stream=None):
+    """Prefill-fused scoring, write half.  k_rows, v_rows [B,n,Hkv,D] go to
+    positions t0.. of k_cache / v_cache [B,S_cap,Hkv,D] (rows at or past len_b
+    skipped) and their key squares are added to k2_state (uint8 device buffer of
+    think_k2_state_bytes, zeroed before a prompt's first chunk)."""
+    _dev(k_rows, v_rows, seq_lens, k_cache, v_cache, k2_state)
+    _i32(seq_lens, "seq_lens")
+    B, S, Hkv, D = k_cache.shape
+    n = k_rows.shape[1]
+    if (tuple(k_rows.shape) != (B, n, Hkv, D) or tuple(v_rows.shape) != (B, n, Hkv, D)
+            or tuple(v_cache.shape) != (B, S, Hkv, D)
+            or len({k_rows.dtype, v_rows.dtype, k_cache.dtype, v_cache.dtype}) != 1):
+        raise ValueError("shape or dtype mismatch between k_rows, v_rows, k_cache and v_cache")
+    dims = make_dims(B, Hkv, Hkv, D, S, _dtype_code(k_cache))
+    _lib.check("think_prefill_write_kv", _lib.lib.think_prefill_write_kv(
+        ctypes.byref(dims), _p(k_rows), _p(v_rows), int(t0), int(n), _p(seq_lens), _p(k_cache),
+        _p(v_cache), _p(k2_state), k2_state.numel() * k2_state.element_size(), _stream(stream)))
+
+
+def think_score_select_k2(dims, k2_state, q_obs, keep=None, *, scores=None, kept_idx=None,
+                          near_tie=None, stream=None):
+    """Scores (fp32 [B,Hkv,D]) from the prefill-write state, no key read; with
+    `keep`, also the kept channels and near-tie flags.  Returns (scores, kept_idx,
+    near_tie), the last two None without `keep`."""
+    _dev(k2_state, q_obs, scores, kept_idx, near_tie)
+    B, Hkv, D = dims.batch, dims.n_kv_heads, dims.head_dim
+    W = q_obs.shape[1]
+    if tuple(q_obs.shape) != (B, W, dims.n_q_heads, D) or _dtype_code(q_obs) != dims.dtype:
+        raise ValueError("q_obs must be [B,W,Hq,D] of the dims' dtype")
+    dev = q_obs.device
+    if scores is None:
+        scores = torch.empty(B, Hkv, D, dtype=torch.float32, device=dev)
+    if keep is not None:
+        if kept_idx is None:
+            kept_idx = torch.empty(B, Hkv, keep, dtype=torch.int32, device=dev)
+        if near_tie is None:
+            near_tie = torch.empty(B, Hkv, dtype=torch.int32, device=dev)
+    _lib.check("think_score_select_k2", _lib.lib.think_score_select_k2(
+        ctypes.byref(dims), _p(k2_state), k2_state.numel() * k2_state.element_size(), _p(q_obs),
+        int(W), int(keep or 0), _p(scores), _p(kept_idx), _p(near_tie), _stream(stream)))
+    return scores, kept_idx, near_tie

@@ -101,9 +101,11 @@ __global__ __launch_bounds__(kThreads) void k_score_partial(
 //       row groups are added in ascending order.
 //  s  = sqrt(K2) * sum_g sqrt(Q2[g]), fp64, stored as fp32; with SELECT the
 //       same workgroup then picks the kept channels (select_row.h).
-template <int DT, bool SELECT>
+// STATE: the sums come from the prefill-write state instead (fp64 slots
+// [B][nsplit][Hkv*D], every slot complete; no length is read).
+template <int DT, bool SELECT, bool STATE>
 __global__ __launch_bounds__(1024) void k_score_finalize(
-        const float* __restrict__ partials, const int32_t* __restrict__ seq_lens, int s_cap,
+        const void* __restrict__ part, const int32_t* __restrict__ seq_lens, int s_cap,
         int tpw, int nsplit, const typename Elem<DT>::T* __restrict__ q_obs, int W, int Hq,
         int Hkv, int D, float* __restrict__ scores, int keep, int32_t* __restrict__ kept_idx,
         int32_t* __restrict__ near_tie) {
@@ -125,14 +127,18 @@ __global__ __launch_bounds__(1024) void k_score_finalize(
     // slots past the length's split count or past the row group are dropped
     // when summed (a dropped slot adds +0.0, so the sums are those of the
     // plain loops).
-    const int len_v = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(seq_lens + b, 4u), 0, 0, 0);
     const int cq = tid % Q, sg = tid / Q;
-    const float4* p = reinterpret_cast<const float4*>(partials + (size_t)b * nsplit * R +
-                                                      (size_t)kv * D) + cq;
+    int len_v = 0;
+    const float4* p = nullptr;
     const size_t sstride = (size_t)R / 4;
     float4 v[8];
+    if constexpr (!STATE) {
+        len_v = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(seq_lens + b, 4u), 0, 0, 0);
+        p = reinterpret_cast<const float4*>(static_cast<const float*>(part) +
+                                            (size_t)b * nsplit * R + (size_t)kv * D) + cq;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = p[(size_t)min(sg + k * SG, nsplit - 1) * sstride];
+        for (int k = 0; k < 8; ++k) v[k] = p[(size_t)min(sg + k * SG, nsplit - 1) * sstride];
+    }
 
     const int GD = G * D, nv = GD / EPV;         // 16-byte vectors per window row
     int RG = nth / nv;
@@ -149,6 +155,34 @@ __global__ __launch_bounds__(1024) void k_score_finalize(
 #pragma unroll
     for (int k = 0; k < 8; ++k) x[k] = qb[(size_t)min(i0 + k, W - 1) * rstride];
 
+    if constexpr (STATE) {
+        // four channels per thread as two 16-byte double pairs per slot
+        const double2* p2 = reinterpret_cast<const double2*>(
+            static_cast<const double*>(part) + (size_t)b * nsplit * R + (size_t)kv * D + 4 * cq);
+        const size_t s2 = (size_t)R / 2;
+        double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+        for (int s0 = sg; s0 < nsplit; s0 += 8 * SG) {
+            double2 w0[8], w1[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const size_t o = (size_t)min(s0 + k * SG, nsplit - 1) * s2;
+                w0[k] = p2[o];
+                w1[k] = p2[o + 1];
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const bool ok = s0 + k * SG < nsplit;
+                a0 += ok ? w0[k].x : 0.0;
+                a1 += ok ? w0[k].y : 0.0;
+                a2 += ok ? w1[k].x : 0.0;
+                a3 += ok ? w1[k].y : 0.0;
+            }
+        }
+        red[sg * D + 4 * cq + 0] = a0;
+        red[sg * D + 4 * cq + 1] = a1;
+        red[sg * D + 4 * cq + 2] = a2;
+        red[sg * D + 4 * cq + 3] = a3;
+    } else {
     const int len_raw = __builtin_amdgcn_readfirstlane(len_v);
     const int len = len_raw < 0 ? 0 : (len_raw > s_cap ? s_cap : len_raw);
     const int ns = (len + tpw - 1) / tpw;
@@ -175,6 +209,7 @@ __global__ __launch_bounds__(1024) void k_score_finalize(
         red[sg * D + 4 * cq + 1] = a1;
         red[sg * D + 4 * cq + 2] = a2;
         red[sg * D + 4 * cq + 3] = a3;
+    }
     }
     // window-query squares of this thread's vector over its rows, in row order
     double acc[EPV];
@@ -260,7 +295,7 @@ hipError_t launch_score(const think_dims& d, const ScoreGeom& g, const void* k_c
     dim3 grid2(d.n_kv_heads, d.batch);
     const int threads2 = Q * sg;
 #define THINK_FINALIZE(DT, SEL, T)                                                               \
-    k_score_finalize<DT, SEL><<<grid2, threads2, 0, s>>>(                                       \
+    k_score_finalize<DT, SEL, false><<<grid2, threads2, 0, s>>>(                                \
         partials, seq_lens, d.seq_capacity, g.tpw, g.nsplit, (const T*)q_obs, W, d.n_q_heads,   \
         d.n_kv_heads, d.head_dim, scores, keep, kept_idx, near_tie)
     if (d.dtype == THINK_BF16) {
@@ -275,6 +310,29 @@ hipError_t launch_score(const think_dims& d, const ScoreGeom& g, const void* k_c
         else THINK_FINALIZE(THINK_F32, false, float);
     }
 #undef THINK_FINALIZE
+    return hipGetLastError();
+}
+
+hipError_t launch_score_k2(const think_dims& d, int nslots, const double* state, const void* q_obs,
+                           int W, float* scores, int keep, int32_t* kept_idx, int32_t* near_tie,
+                           hipStream_t s) {
+    const int Q = d.head_dim / 4;
+    int sg = 1024 / Q;
+    if (sg > 64) sg = 64;
+    dim3 grid2(d.n_kv_heads, d.batch);
+    const int threads2 = Q * sg;
+#define THINK_FINALIZE_K2(DT, SEL, T)                                                            \
+    k_score_finalize<DT, SEL, true><<<grid2, threads2, 0, s>>>(                                 \
+        state, nullptr, d.seq_capacity, 1, nslots, (const T*)q_obs, W, d.n_q_heads,             \
+        d.n_kv_heads, d.head_dim, scores, keep, kept_idx, near_tie)
+    if (d.dtype == THINK_BF16) {
+        if (kept_idx) THINK_FINALIZE_K2(THINK_BF16, true, uint16_t);
+        else THINK_FINALIZE_K2(THINK_BF16, false, uint16_t);
+    } else {
+        if (kept_idx) THINK_FINALIZE_K2(THINK_F32, true, float);
+        else THINK_FINALIZE_K2(THINK_F32, false, float);
+    }
+#undef THINK_FINALIZE_K2
     return hipGetLastError();
 }
 

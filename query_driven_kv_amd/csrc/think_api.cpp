@@ -194,6 +194,44 @@ int think_append_kv(const think_dims* d, const void* k_new, const void* v_new, i
                                              v_cache, (hipStream_t)stream));
 }
 
+size_t think_k2_state_bytes(const think_dims* d) {
+    if (check_dims(d) != THINK_OK) return 0;
+    return thinkkv::k2_geom(*d).bytes;
+}
+
+int think_prefill_write_kv(const think_dims* d, const void* k_rows, const void* v_rows, int32_t t0,
+                           int32_t n_rows, const int32_t* seq_lens, void* k_cache, void* v_cache,
+                           void* k2_state, size_t k2_state_bytes, void* stream) {
+    int st = check_dims(d);
+    if (st != THINK_OK) return st;
+    if (!k_rows || !v_rows || !seq_lens || !k_cache || !v_cache) return THINK_ERR_NULL;
+    if (t0 < 0 || n_rows < 0) return THINK_ERR_SHAPE;
+    if (!aligned16(k_rows) || !aligned16(v_rows) || !aligned16(k_cache) || !aligned16(v_cache))
+        return THINK_ERR_UNSUPPORTED;
+    const thinkkv::K2Geom g = thinkkv::k2_geom(*d);
+    if (!k2_state || k2_state_bytes < g.bytes || !aligned16(k2_state)) return THINK_ERR_WORKSPACE;
+    if (n_rows == 0) return THINK_OK;
+    return hip_status(thinkkv::launch_prefill_write(*d, g, k_rows, v_rows, t0, n_rows, seq_lens,
+                                                    k_cache, v_cache, (double*)k2_state,
+                                                    (hipStream_t)stream));
+}
+
+int think_score_select_k2(const think_dims* d, const void* k2_state, size_t k2_state_bytes,
+                          const void* q_obs, int32_t obs_window, int32_t keep, float* scores,
+                          int32_t* kept_idx, int32_t* near_tie, void* stream) {
+    int st = check_dims(d);
+    if (st != THINK_OK) return st;
+    if (!q_obs || (!scores && !kept_idx)) return THINK_ERR_NULL;
+    if (obs_window < 1) return THINK_ERR_SHAPE;
+    if (kept_idx && (keep < 1 || keep > d->head_dim)) return THINK_ERR_KEEP;
+    if (!aligned16(q_obs)) return THINK_ERR_UNSUPPORTED;
+    const thinkkv::K2Geom g = thinkkv::k2_geom(*d);
+    if (!k2_state || k2_state_bytes < g.bytes || !aligned16(k2_state)) return THINK_ERR_WORKSPACE;
+    return hip_status(thinkkv::launch_score_k2(*d, g.nslots, (const double*)k2_state, q_obs,
+                                               obs_window, scores, keep, kept_idx, near_tie,
+                                               (hipStream_t)stream));
+}
+
 const char* think_status_string(int status) {
     switch (status) {
         case THINK_OK: return "ok";

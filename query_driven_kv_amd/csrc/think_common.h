@@ -106,6 +106,15 @@ struct DecodeGeom {
 };
 DecodeGeom decode_geom(const think_dims& d, int keep);
 
+// Prefill-write state: fp64 sums of squares per (b, slot, channel).
+struct K2Geom {
+    int nvec;        // 16-byte vectors per token row
+    int ncg;         // column groups of <= 256 vectors
+    int nslots;      // row ranges per chunk (state slots per sequence)
+    size_t bytes;    // state [B][nslots][Hkv*D] fp64
+};
+K2Geom k2_geom(const think_dims& d);
+
 struct CompactGeom {
     int tile;        // tokens per workgroup
     size_t lds;      // dynamic LDS bytes
@@ -124,6 +133,12 @@ hipError_t launch_select(const think_dims& d, const float* scores, int keep, int
 hipError_t launch_compact(const think_dims& d, const CompactGeom& g, const void* k_cache,
                           const int32_t* seq_lens, const int32_t* kept_idx, int keep,
                           void* k_thin, hipStream_t s);
+hipError_t launch_prefill_write(const think_dims& d, const K2Geom& g, const void* k_rows,
+                                const void* v_rows, int t0, int n_rows, const int32_t* seq_lens,
+                                void* k_cache, void* v_cache, double* state, hipStream_t s);
+hipError_t launch_score_k2(const think_dims& d, int nslots, const double* state, const void* q_obs,
+                           int W, float* scores, int keep, int32_t* kept_idx, int32_t* near_tie,
+                           hipStream_t s);
 hipError_t launch_append(const think_dims& d, const void* k_new, const void* v_new,
                          int32_t* seq_lens, const int32_t* kept_idx, int keep, void* k_thin,
                          void* v_cache, hipStream_t s);

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_header_declarations_are_all_exported(L):
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 17
     assert sorted(L.EXPORTS) == names
     so = ctypes.CDLL(L.LIB_PATH)
     for n in names:
@@ -42,7 +42,7 @@ def test_only_the_abi_is_exported(L):
 
 def test_version_and_keep_rounding(L):
     lib = L.lib
-    assert lib.think_abi_version() == 2
+    assert lib.think_abi_version() == 3
     assert [lib.think_keep_from_ratio(128, r) for r in (0.4, 0.6, 0.5)] == [77, 51, 64]
     assert lib.think_keep_from_ratio(16, 0.5) == 8
     assert lib.think_keep_from_ratio(128, 0.0) == 128
@@ -95,6 +95,38 @@ def test_score_rejects_bad_dims(L, kw, status):
                                    FAKE, 1 << 30, None) == status
     assert L.lib.think_append_kv(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 8, FAKE, FAKE,
                                  None) == status
+    assert L.lib.think_prefill_write_kv(ctypes.byref(d), FAKE, FAKE, 0, 16, FAKE, FAKE, FAKE,
+                                        FAKE, 1 << 30, None) == status
+    assert L.lib.think_score_select_k2(ctypes.byref(d), FAKE, 1 << 30, FAKE, 8, 8, FAKE, FAKE,
+                                       None, None) == status
+    assert L.lib.think_k2_state_bytes(ctypes.byref(d)) == 0
+
+
+def test_prefill_and_k2_score_validation(L):
+    lib = L.lib
+    d = dims(L)
+    big = 1 << 30
+    need = lib.think_k2_state_bytes(ctypes.byref(d))
+    assert need > 0 and need % 16 == 0
+    assert lib.think_k2_state_bytes(None) == 0
+    w = lib.think_prefill_write_kv
+    assert w(ctypes.byref(d), None, FAKE, 0, 8, FAKE, FAKE, FAKE, FAKE, big, None) == -1
+    assert w(ctypes.byref(d), FAKE, FAKE, 0, 8, None, FAKE, FAKE, FAKE, big, None) == -1
+    assert w(ctypes.byref(d), FAKE, FAKE, -1, 8, FAKE, FAKE, FAKE, FAKE, big, None) == -2
+    assert w(ctypes.byref(d), FAKE, FAKE, 0, -8, FAKE, FAKE, FAKE, FAKE, big, None) == -2
+    assert w(ctypes.byref(d), FAKE, FAKE, 0, 8, FAKE, FAKE, FAKE, None, big, None) == -6
+    assert w(ctypes.byref(d), FAKE, FAKE, 0, 8, FAKE, FAKE, FAKE, FAKE, need - 16, None) == -6
+    assert w(ctypes.byref(d), ctypes.c_void_p(0x100008), FAKE, 0, 8, FAKE, FAKE, FAKE, FAKE, big,
+             None) == -5
+    assert w(ctypes.byref(d), FAKE, FAKE, 0, 0, FAKE, FAKE, FAKE, FAKE, big, None) == 0  # nothing to do
+    k = lib.think_score_select_k2
+    assert k(ctypes.byref(d), FAKE, big, None, 8, 8, FAKE, FAKE, None, None) == -1
+    assert k(ctypes.byref(d), FAKE, big, FAKE, 8, 8, None, None, None, None) == -1
+    assert k(ctypes.byref(d), FAKE, big, FAKE, 0, 8, FAKE, FAKE, None, None) == -2
+    assert k(ctypes.byref(d), FAKE, big, FAKE, 8, 0, FAKE, FAKE, None, None) == -3
+    assert k(ctypes.byref(d), FAKE, big, FAKE, 8, 129, None, FAKE, None, None) == -3
+    assert k(ctypes.byref(d), FAKE, 16, FAKE, 8, 8, FAKE, FAKE, None, None) == -6
+    assert k(ctypes.byref(d), None, big, FAKE, 8, 8, FAKE, FAKE, None, None) == -6
 
 
 def test_append_validation(L):
