@@ -253,6 +253,56 @@ def append_time(cfg, torch, qdk, dev, calls=512):
     return e0.elapsed_time(e1) * 1e3 / (calls - 1), B * Hkv * (2 * D + keep + D) * e
 
 
+def prefill_time(wl, torch, qdk, chunk=8192, reps=3):
+    """Prefill-fused scoring on layer 0 of a batch-1 workload: the prompt's K/V
+    rows (the resident caches serve as the rows a prefill would produce; with
+    one sequence a range of cache rows is a contiguous chunk) are written
+    into scratch caches chunk by chunk while their key sums are gathered, then
+    the scores and selection come from the gathered sums and the key cache is
+    compacted.  Returns microseconds for (the whole write, score+select from the
+    sums, compaction) of one layer, each the mean of `reps` runs."""
+    from query_driven_kv_amd import _lib
+    P = ctypes.c_void_p
+    cfg, e = wl.cfg, wl.layers[0]
+    B, S, Hkv, D, keep, W = (cfg.batch, cfg.seq_capacity, cfg.n_kv_heads, cfg.head_dim, cfg.keep,
+                             cfg.obs_window)
+    kc, vc = torch.empty_like(e["k"]), torch.empty_like(e["v"])
+    thin = torch.empty_like(e["thin"])
+    idx, tie = torch.empty_like(e["idx"]), torch.empty_like(e["tie"])
+    dims = wl.dims
+    state = torch.zeros(qdk.think_k2_state_bytes(dims), dtype=torch.uint8, device=e["k"].device)
+    sp = P(torch.cuda.current_stream().cuda_stream)
+    lib = _lib.lib
+    row = Hkv * D * e["k"].element_size()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    t_w, t_s, t_c = [], [], []
+    for _ in range(reps + 1):
+        state.zero_()
+        ev[0].record()
+        for t0 in range(0, S, chunk):
+            n = min(chunk, S - t0)
+            off = t0 * row
+            _lib.check("think_prefill_write_kv", lib.think_prefill_write_kv(
+                ctypes.byref(dims), P(e["k"].data_ptr() + off), P(e["v"].data_ptr() + off), t0, n,
+                P(e["lens"].data_ptr()), P(kc.data_ptr()), P(vc.data_ptr()), P(state.data_ptr()),
+                state.numel(), sp))
+        ev[1].record()
+        _lib.check("think_score_select_k2", lib.think_score_select_k2(
+            ctypes.byref(dims), P(state.data_ptr()), state.numel(), P(e["qo"].data_ptr()), W, keep,
+            None, P(idx.data_ptr()), P(tie.data_ptr()), sp))
+        ev[2].record()
+        _lib.check("think_compact_k", lib.think_compact_k(
+            ctypes.byref(dims), P(kc.data_ptr()), P(e["lens"].data_ptr()), P(idx.data_ptr()), keep,
+            P(thin.data_ptr()), sp))
+        ev[3].record()
+        torch.cuda.synchronize()
+        t_w.append(ev[0].elapsed_time(ev[1]) * 1e3)
+        t_s.append(ev[1].elapsed_time(ev[2]) * 1e3)
+        t_c.append(ev[2].elapsed_time(ev[3]) * 1e3)
+    assert torch.equal(idx, e["idx"]), "selection from the gathered sums differs from the cache path"
+    return float(np.mean(t_w[1:])), float(np.mean(t_s[1:])), float(np.mean(t_c[1:]))
+
+
 def decode_source_hash():
     import hashlib
     h = hashlib.sha256()
@@ -393,6 +443,25 @@ def main():
     achieved = bm["dec_call"] / (part_us * 1e-6) / 1e9 if n_part else None
     app_us, app_bytes = append_time(cfg, torch, qdk, dev)
     log(f"decode-time append: {app_us:.2f} us per call")
+    pre = None
+    if cfg.batch == 1:
+        pw_us, ps_us, pc_us = prefill_time(wl, torch, qdk)
+        e = 2 if cfg.dtype == "bf16" else 4
+        K = tok * cfg.n_kv_heads * cfg.head_dim * e
+        Kt = tok * cfg.n_kv_heads * cfg.keep * e
+        Qw = cfg.obs_window * cfg.n_q_heads * cfg.head_dim * e
+        pre = {"write_us_per_layer": round(pw_us, 1),
+               "write_GBps": round(4 * K / (pw_us * 1e-6) / 1e9, 1),
+               "score_select_from_sums_us": round(ps_us, 2),
+               "compact_us": round(pc_us, 1),
+               "prune_after_prefill_GBps": round((K + Kt + Qw) / ((ps_us + pc_us) * 1e-6) / 1e9, 1),
+               "prune_after_prefill_pct_of_peak":
+                   round(100 * (K + Kt + Qw) / ((ps_us + pc_us) * 1e-6) / 1e9 / PEAK_GBS, 2),
+               "note": "layer 0: prompt written in 8192-row chunks (reads and writes K and V: "
+                       "4|K| bytes) gathering the key sums; then scores+selection from the sums "
+                       "and compaction, |K| + |K_thin| + |Q_w| bytes (one read of K)"}
+        log(f"prefill-fused scoring: write {pw_us:.1f} us, score from sums {ps_us:.2f} us, "
+            f"compact {pc_us:.1f} us per layer")
     traffic, traffic_src = committed_traffic(cfg.name)
 
     result = {
@@ -426,6 +495,7 @@ def main():
                        "us_per_call": round(dec_call_us, 2),
                        "kv_tokens_per_s": float(f"{tok * n_dec / (dec_ms / 1e3):.4g}"),
                        "bytes_per_call": bm["dec_call"]},
+            "prefill_fused_scoring": pre,
             "append": {"us_per_call": round(app_us, 2), "bytes_per_call": app_bytes,
                        "note": "think_append_kv, timed apart from the step (the workload's "
                                "caches are full)"},
