@@ -116,13 +116,15 @@ __global__ __launch_bounds__(kThreads) void k_decode_partial(
     }
 }
 
-// Merge the chunks of one (b, h).  The block is D x SG threads: sub-group sg
-// merges a contiguous range of the nsplit chunk slots in ascending order,
-// eight at a time with a running maximum, then the SG results are merged in
-// ascending sg order.  Fixed order, so the result is bitwise reproducible.
-// The ranges are fixed by nsplit rather than by the length, so the record
-// loads do not wait for the length load; slots at or past the sequence's
-// chunk count are dropped after loading (their contents are never used).
+// Merge the chunks of one (b, h).  The block is (D/4) x SG threads, each
+// thread owning four output columns (one 16-byte record load per slot):
+// sub-group sg merges a contiguous range of the nsplit chunk slots in
+// ascending order, eight at a time with a running maximum, then the SG results
+// are merged in ascending sg order.  Fixed order, so the result is bitwise
+// reproducible.  The ranges are fixed by nsplit rather than by the length, so
+// the record loads do not wait for the length load; slots at or past the
+// sequence's chunk count are dropped after loading (their contents are never
+// used).
 template <int DT>
 __global__ __launch_bounds__(1024) void k_decode_combine(
         const float* __restrict__ partials, const int32_t* __restrict__ seq_lens, int s_cap,
@@ -131,49 +133,58 @@ __global__ __launch_bounds__(1024) void k_decode_combine(
     constexpr float kNone = -3.402823466e38f;   // finite stand-in for an empty maximum
     const int h = blockIdx.x, b = blockIdx.y, Hq = gridDim.x;
     const int tid = threadIdx.x;
-    const int d = tid % D, sg = tid / D;
+    const int D4 = D >> 2;
+    const int d4 = tid % D4, sg = tid / D4;
     const float* base = partials + ((size_t)b * Hq + h) * nsplit * rec;
-    // sg_count <= 16 and nsplit <= 2^21, so 32-bit products suffice
     const int lo = (int)((unsigned)(sg * nsplit) / (unsigned)sg_count);
     const int hi = (int)((unsigned)((sg + 1) * nsplit) / (unsigned)sg_count);
     int len_raw = seq_lens[b];
-    float M = kNone, L = 0.0f, O = 0.0f;
+    float M = kNone, L = 0.0f;
+    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s0 = lo; s0 < hi; s0 += 8) {
-        float mv[8], lv[8], ov[8];
+        float2 ml[8];
+        float4 ov[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const float* r = base + (size_t)min(s0 + k, nsplit - 1) * rec;
-            mv[k] = r[0];
-            lv[k] = r[1];
-            ov[k] = r[4 + d];
+            ml[k] = *reinterpret_cast<const float2*>(r);
+            ov[k] = *reinterpret_cast<const float4*>(r + 4 + 4 * d4);
         }
         // the record loads above are issued before the length is waited on
         asm volatile("" : "+s"(len_raw)::"memory");
         const int len = len_raw < 0 ? 0 : (len_raw > s_cap ? s_cap : len_raw);
         const int ns = (len + chunk - 1) / chunk;
+        float mv[8], lv[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const bool ok = s0 + k < hi && s0 + k < ns;
-            mv[k] = ok ? mv[k] : kNone;
-            lv[k] = ok ? lv[k] : 0.0f;
-            ov[k] = ok ? ov[k] : 0.0f;
+            mv[k] = ok ? ml[k].x : kNone;
+            lv[k] = ok ? ml[k].y : 0.0f;
+            if (!ok) ov[k] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
         float Mn = M;
 #pragma unroll
         for (int k = 0; k < 8; ++k) Mn = fmaxf(Mn, mv[k]);
         const float f = expf(M - Mn);
         L *= f;
-        O *= f;
+        O.x *= f;
+        O.y *= f;
+        O.z *= f;
+        O.w *= f;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const float w = expf(mv[k] - Mn);
             L = fmaf(w, lv[k], L);
-            O = fmaf(w, ov[k], O);
+            O.x = fmaf(w, ov[k].x, O.x);
+            O.y = fmaf(w, ov[k].y, O.y);
+            O.z = fmaf(w, ov[k].z, O.z);
+            O.w = fmaf(w, ov[k].w, O.w);
         }
         M = Mn;
     }
-    __shared__ float sM[64], sL[64], sO[1024];
-    if (d == 0) {
+    __shared__ float sM[64], sL[64];
+    __shared__ float4 sO[1024];
+    if (d4 == 0) {
         sM[sg] = M;
         sL[sg] = L;
     }
@@ -182,13 +193,23 @@ __global__ __launch_bounds__(1024) void k_decode_combine(
     if (sg == 0) {
         float MM = sM[0];
         for (int r = 1; r < sg_count; ++r) MM = fmaxf(MM, sM[r]);
-        float LL = 0.0f, OO = 0.0f;
+        float LL = 0.0f;
+        float4 OO = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int r = 0; r < sg_count; ++r) {
             const float f = sL[r] > 0.0f ? expf(sM[r] - MM) : 0.0f;
+            const float4 o = sO[r * D4 + d4];
             LL = fmaf(f, sL[r], LL);
-            OO = fmaf(f, sO[r * D + d], OO);
+            OO.x = fmaf(f, o.x, OO.x);
+            OO.y = fmaf(f, o.y, OO.y);
+            OO.z = fmaf(f, o.z, OO.z);
+            OO.w = fmaf(f, o.w, OO.w);
         }
-        E::store(out, ((size_t)b * Hq + h) * D + d, LL > 0.0f ? OO / LL : 0.0f);
+        const bool any = LL > 0.0f;
+        const size_t o0 = ((size_t)b * Hq + h) * D + 4 * d4;
+        E::store(out, o0 + 0, any ? OO.x / LL : 0.0f);
+        E::store(out, o0 + 1, any ? OO.y / LL : 0.0f);
+        E::store(out, o0 + 2, any ? OO.z / LL : 0.0f);
+        E::store(out, o0 + 3, any ? OO.w / LL : 0.0f);
     }
 }
 
@@ -230,7 +251,7 @@ hipError_t launch_decode_combine(const think_dims& d, const DecodeGeom& g, const
     dim3 cgrid(d.n_q_heads, d.batch);
     int sg_count = 1024 / d.head_dim;
     if (sg_count > 16) sg_count = 16;
-    const int cthreads = d.head_dim * sg_count;
+    const int cthreads = d.head_dim / 4 * sg_count;
     if (d.dtype == THINK_BF16)
         k_decode_combine<THINK_BF16><<<cgrid, cthreads, 0, s>>>(
             partials, seq_lens, d.seq_capacity, g.chunk, g.nsplit, g.rec, d.head_dim, sg_count,
