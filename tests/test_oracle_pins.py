@@ -268,7 +268,7 @@ def test_greedy_chain_residual_nonincreasing_on_seeded_inputs():
     does not increase on these seeded Gaussian inputs (an empirical property,
     see test_residual_monotone_is_not_a_theorem); brute force reports how
     close greedy comes at D=12."""
-    ratios, optimal = [], 0
+    ratios, ranks, optimal = [], [], 0
     for seed in range(100):
         rng = np.random.default_rng(1000 + seed)
         D = 12
@@ -287,7 +287,11 @@ def test_greedy_chain_residual_nonincreasing_on_seeded_inputs():
         bf = oracle.bruteforce(Qf, Kf, 6, candidate=idx[0, 0])
         assert bf["r_opt"] <= bf["r_candidate"] * (1 + 1e-12)
         ratios.append(bf["r_candidate"] / bf["r_opt"])
+        ranks.append(bf["candidate_rank"])
         optimal += bf["candidate_rank"] == 0
+    print(f"\n[report] greedy vs brute force at D=12, keep=6 over 100 draws: optimal in "
+          f"{optimal}, residual ratio median {np.median(ratios):.4f} max {max(ratios):.4f}, "
+          f"rank among C(12,6)=924 subsets median {int(np.median(ranks))} max {max(ranks)}")
     assert optimal >= 50          # greedy is the exact optimum on most draws
     assert max(ratios) < 1.5
 
@@ -517,3 +521,25 @@ def test_score_from_gathered_sums_matches_the_definition():
     s = oracle.score_from_k2(k2, L["q_obs"])
     ref = _def_scores(L["k_cache"], lens, L["q_obs"], cfg.group)
     np.testing.assert_allclose(s, ref, rtol=1e-12, atol=0)
+
+
+def test_gqa_reading_report():
+    """Report, not a pin: how often the stacked-Frobenius reading of the
+    grouped-query aggregation (root-sum-square over the group's query heads)
+    would keep a different channel set than the sum reading, on seeded caches
+    shaped like the 32K GQA workload (shorter).  The sum reading is the one the
+    path implements; the two share the key factor, so they differ only through
+    the query heads' spread."""
+    cfg = kvsynth.custom("gqa-report", batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                         seq_capacity=2048, obs_window=32, keep=64, dtype="bf16", lowrank=32,
+                         n_outliers=4, cfg_id=3)
+    differ, total = 0, 0
+    for layer in range(4):
+        L = kvsynth.make_layer(cfg, layer)
+        a, _ = oracle.select(oracle.score(L["k_cache"], L["seq_lens"], L["q_obs"]), 64)
+        b, _ = oracle.select(oracle.score_rss(L["k_cache"], L["seq_lens"], L["q_obs"]), 64)
+        differ += int((a != b).any(axis=-1).sum())
+        total += a.shape[0] * a.shape[1]
+    print(f"\n[report] GQA sum vs root-sum-square reading: kept sets differ in {differ} of "
+          f"{total} (b, kv) heads")
+    assert 0 <= differ <= total
