@@ -191,7 +191,8 @@ class Workload:
                 d, lens, keep, out, ws, wsn, stream))
             k += 1
         torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3, n
+        us = np.array([a.elapsed_time(b) for a, b in ev]) * 1e3
+        return float(us.mean()), n, [round(float(x), 2) for x in np.percentile(us, [10, 50, 90])]
 
     def decode(self, stream, steps=None):
         from query_driven_kv_amd import _lib
@@ -351,8 +352,14 @@ def cpu_baseline(wl, budget_s):
         steps += 1
     total_bytes = bm["sc_layer"] + steps * bm["dec_call"]
     total_s = t_sc + t_dec
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(total_bytes / total_s / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu": model,
             "sample": (f"layer 0 of {cfg.name}: score+select+compact once ({t_sc:.2f}s) and "
                        f"{steps} decode steps ({t_dec:.2f}s); fp64 C oracle, OpenMP over "
                        f"(batch, head) pairs, {threads} threads"),
@@ -436,9 +443,9 @@ def main():
     # the dominant kernel's own launch duration, live, with HIP events (a
     # separate pass after the timed region, so the events do not perturb it)
     if args.no_kernel_timing:
-        part_us, n_part = float("nan"), 0
+        part_us, n_part, part_pct = float("nan"), 0, None
     else:
-        part_us, n_part = wl.decode_kernel_times(sp, torch)
+        part_us, n_part, part_pct = wl.decode_kernel_times(sp, torch)
         log(f"chunk-pass kernel: {part_us:.2f} us mean over {n_part} launches")
     achieved = bm["dec_call"] / (part_us * 1e-6) / 1e9 if n_part else None
     app_us, app_bytes = append_time(cfg, torch, qdk, dev)
@@ -507,6 +514,7 @@ def main():
                      "traffic": traffic,
                      "algorithmic_bytes_per_launch": bm["dec_call"],
                      "launch_us": round(part_us, 2) if n_part else None,
+                     "launch_us_p10_p50_p90": part_pct,
                      "timing": (f"HIP events on the launch stream around each of the {n_part} "
                                 f"chunk-pass launches of one step, after the timed steps"),
                      "traffic_source": traffic_src},
