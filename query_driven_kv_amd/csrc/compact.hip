@@ -83,8 +83,11 @@ CompactGeom compact_geom(const think_dims& d, int keep) {
     CompactGeom g{};
     const int row_bytes = d.n_kv_heads * d.head_dim * elem_bytes(d.dtype);
     // 16 KiB tiles (8 rows of a 2 KiB row): enough workgroups per CU to keep
-    // the loads and stores of several tiles in flight
+    // the loads and stores of several tiles in flight.  Wide rows (many kv
+    // heads) take at least 4 rows (up to 64 KiB), so the per-workgroup source
+    // map of Hkv*keep kept channels is built for enough data to pay for itself.
     int tile = 16384 / row_bytes;
+    if (tile < 4) tile = 65536 / row_bytes < 4 ? 65536 / row_bytes : 4;
     if (tile > 64) tile = 64;
     if (tile < 1) tile = 1;
     g.tile = tile;

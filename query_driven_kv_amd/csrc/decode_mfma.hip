@@ -407,7 +407,9 @@ bool mfma_decode_supported(const think_dims& d, int keep) {
 }
 
 // Tokens per workgroup: a multiple of 128 (one 32-token step per wave), sized
-// for about 512 workgroups (two per CU) and at most 256 chunks per sequence.
+// for about 512 workgroups (two per CU) and at most 256 chunks per sequence,
+// and at least 512 (four steps per wave) so the prologue and the merge stay
+// small next to the stream when there are many kv heads and few tokens.
 int mfma_decode_chunk(const think_dims& d, int keep) {
     (void)keep;
     const int64_t work = (int64_t)d.seq_capacity * d.n_kv_heads * d.batch;
@@ -415,7 +417,7 @@ int mfma_decode_chunk(const think_dims& d, int keep) {
     const int64_t min_chunk = ((int64_t)d.seq_capacity + 255) / 256;
     if (chunk < min_chunk) chunk = min_chunk;
     chunk = (chunk + 127) / 128 * 128;
-    if (chunk < 128) chunk = 128;
+    if (chunk < 512) chunk = 512;
     return (int)chunk;
 }
 
