@@ -81,16 +81,20 @@ __device__ __forceinline__ uint4 v_column(const uint4 (&v)[8]) {
 }
 
 // K_thin octets (8 channels, 16 bytes of one head row).  KAL = 8: head rows
-// are 16-byte aligned and an octet is one aligned dwordx4.  KAL = 2: rows are
-// 4-byte aligned; the octet is one dwordx4 at a 4-byte aligned offset and the
-// channels past keep are masked.  KAL = 1: rows are only 2-byte aligned; the
-// dwordx4 at the dword boundary at or below the octet and the dword after it
-// are loaded, and the octet is re-paired from them with a per-lane byte shift
-// (0 or 2) when the step computes.  Every case is one or two wide loads per
-// octet, never element loads.
+// are 16-byte aligned and an octet is one aligned dwordx4.  KAL = 0 (keep not
+// a multiple of 8, at most 96): each lane loads the 16-byte aligned chunks
+// 4*jb + q4 of its token row (lanes q4 = 0 one more, chunk 4*KB); the octet of
+// block jb spans that chunk and the next one, which the lane 16 above holds,
+// so a lane rotation brings it in and a per-lane byte shift (the row's offset
+// inside its first chunk, the same in every step) cuts the octet out.  Every
+// load is an aligned dwordx4.  KAL = 2 / 1 (keep above 96, where the extra
+// chunk costs too many registers): the dwordx4 at the octet's own 4-byte
+// aligned offset (even keep), or at the dword boundary below it plus the dword
+// after it with a byte shift of 0 or 2 (odd keep).  Channels past keep are
+// masked in every case but KAL = 8.
 template <int KB, int KAL>
 struct Frag {
-    uint4 k[2][KB];                      // token half x 32-channel block
+    uint4 k[2][KAL == 0 ? KB + 1 : KB];  // token half x 32-channel block (KAL 0: x chunk)
     uint32_t ky[2][KAL == 1 ? KB : 1];   // KAL 1: the dword after each dwordx4
     uint4 v[8];                          // V rows of this lane's 8 tokens (16 bytes each)
 };
@@ -99,14 +103,17 @@ struct Frag {
 // the step's K_thin / V descriptor bases).
 template <int KB>
 struct LaneOffsets {
-    uint32_t k[2][KB];   // dword-aligned offset of the octet's dwordx4; kOff when past keep
-    uint32_t ks[2][KB];  // byte shift of the octet inside that dwordx4 (KAL 1)
-    uint4 kmask[KB];     // channel mask of the octet (KAL 2 / 1)
-    uint32_t v[8];       // V row of this lane's token i, channel octet n16
+    uint32_t k[2][KB];       // dword-aligned offset of the octet's dwordx4; kOff when past keep
+    uint32_t ks[2][KB];      // byte shift of the octet inside that dwordx4 (KAL 1)
+    uint32_t kc[2][KB + 1];  // KAL 0: offset of chunk 4*jb + q4; kOff when not needed
+    uint32_t kr[2];          // KAL 0: the token row's byte offset inside its first chunk
+    uint4 kmask[KB];         // channel mask of the octet (all but KAL 8)
+    uint32_t v[8];           // V row of this lane's token i, channel octet n16
 };
 
 // `delta` is the K_thin descriptor base's distance below the step's first
-// row of this head (0, or 2 when that row is not 4-byte aligned).
+// row of this head: the row's offset from a 16-byte boundary (KAL 0), from a
+// 4-byte boundary (KAL 1), else 0.
 template <int KB>
 __device__ __forceinline__ LaneOffsets<KB> lane_offsets(int keep, size_t kt_row, size_t v_row,
                                                         int n16, int q4, uint32_t delta) {
@@ -128,6 +135,21 @@ __device__ __forceinline__ LaneOffsets<KB> lane_offsets(int keep, size_t kt_row,
         }
         lo.kmask[jb] = make_uint4(mw[0], mw[1], mw[2], mw[3]);
     }
+    // KAL 0: a chunk is loaded if it starts before the row's last kept channel
+    // ends (it then lies inside the descriptor's range, which is rounded up to
+    // 16 bytes)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t row = (uint32_t)((16 * h + n16) * kt_row * 2) + delta;
+        const uint32_t r = row & 15u, al = row & ~15u;
+        lo.kr[h] = r;
+#pragma unroll
+        for (int jb = 0; jb <= KB; ++jb) {
+            const uint32_t k = 4u * jb + q4;
+            const bool need = 16u * k < r + 2u * (uint32_t)keep && (jb < KB || q4 == 0);
+            lo.kc[h][jb] = need ? al + 16u * k : kOff;
+        }
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i)
         lo.v[i] = (uint32_t)(((4 * q4 + (i & 3) + 16 * (i >> 2)) * v_row + 8 * n16) * 2);
@@ -139,15 +161,22 @@ __device__ __forceinline__ LaneOffsets<KB> lane_offsets(int keep, size_t kt_row,
 template <int KB, int KAL>
 __device__ __forceinline__ void load_step(Frag<KB, KAL>& f, __amdgpu_buffer_rsrc_t rk,
                                           __amdgpu_buffer_rsrc_t rv, const LaneOffsets<KB>& lo) {
+    if constexpr (KAL == 0) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int jb = 0; jb < KB; ++jb) {
-            f.k[h][jb] = ldb_stream(rk, lo.k[h][jb]);
-            if constexpr (KAL == 1)
-                f.ky[h][jb] = __builtin_amdgcn_raw_buffer_load_b32(rk, (int)(lo.k[h][jb] + 16u), 0,
-                                                                   kNonTemporal);
-        }
+            for (int jb = 0; jb <= KB; ++jb) f.k[h][jb] = ldb_stream(rk, lo.kc[h][jb]);
+    } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int jb = 0; jb < KB; ++jb) {
+                f.k[h][jb] = ldb_stream(rk, lo.k[h][jb]);
+                if constexpr (KAL == 1)
+                    f.ky[h][jb] = __builtin_amdgcn_raw_buffer_load_b32(
+                            rk, (int)(lo.k[h][jb] + 16u), 0, kNonTemporal);
+            }
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) f.v[i] = ldb_stream(rv, lo.v[i]);
 }
@@ -172,16 +201,67 @@ __device__ __forceinline__ uint4 k_operand(const Frag<KB, KAL>& f, const LaneOff
     }
 }
 
+__device__ __forceinline__ uint32_t pick(bool c, uint32_t a, uint32_t b) { return c ? a : b; }
+
+// Bytes [r, r + 16) of the 32-byte window (lo, hi), r in [0, 16): two dword
+// selects (by 8 and by 4 bytes) and a byte funnel shift.  Written as scalar
+// selects so that no indexed private array is formed.
+__device__ __forceinline__ uint4 window16(const uint4& lo, const uint4& hi, uint32_t r) {
+    const bool s8 = (r & 8u) != 0, s4 = (r & 4u) != 0;
+    const uint32_t rb = r & 3u;
+    const uint32_t u0 = pick(s8, lo.z, lo.x), u1 = pick(s8, lo.w, lo.y), u2 = pick(s8, hi.x, lo.z),
+                   u3 = pick(s8, hi.y, lo.w), u4 = pick(s8, hi.z, hi.x), u5 = pick(s8, hi.w, hi.y);
+    const uint32_t a0 = pick(s4, u1, u0), a1 = pick(s4, u2, u1), a2 = pick(s4, u3, u2),
+                   a3 = pick(s4, u4, u3), a4 = pick(s4, u5, u4);
+    return make_uint4(__builtin_amdgcn_alignbyte(a1, a0, rb), __builtin_amdgcn_alignbyte(a2, a1, rb),
+                      __builtin_amdgcn_alignbyte(a3, a2, rb), __builtin_amdgcn_alignbyte(a4, a3, rb));
+}
+
+// x of the lane 16 above (wrapping within the wave).
+__device__ __forceinline__ uint4 from_lane_plus16(const uint4& x, int lane) {
+    const int src = ((lane + 16) & 63) << 2;
+    return make_uint4(__builtin_amdgcn_ds_bpermute(src, (int)x.x),
+                      __builtin_amdgcn_ds_bpermute(src, (int)x.y),
+                      __builtin_amdgcn_ds_bpermute(src, (int)x.z),
+                      __builtin_amdgcn_ds_bpermute(src, (int)x.w));
+}
+
 // Logits, online softmax and the value product of one 32-token step.
 template <int KB, int KAL>
 __device__ __forceinline__ void compute_step(const Frag<KB, KAL>& f, const LaneOffsets<KB>& lo,
                                              int nt, float scale, const uint4 (&qB)[KB], int q4,
                                              f32x4 (&O)[8], float& m, float& l) {
     f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (KAL == 0) {
+        // chunk 4*jb + q4 + 1 is in the lane 16 above: its chunk of block jb,
+        // or of block jb + 1 (chunk 0) when q4 = 3
+        const int lane = threadIdx.x & 63;
+        const bool wrap = q4 == 3;
 #pragma unroll
-    for (int jb = 0; jb < KB; ++jb) {
-        c0 = mfma(k_operand<KB, KAL>(f, lo, 0, jb), qB[jb], c0);
-        c1 = mfma(k_operand<KB, KAL>(f, lo, 1, jb), qB[jb], c1);
+        for (int h = 0; h < 2; ++h) {
+            uint4 y[KB + 1];
+#pragma unroll
+            for (int jb = 0; jb <= KB; ++jb) y[jb] = from_lane_plus16(f.k[h][jb], lane);
+#pragma unroll
+            for (int jb = 0; jb < KB; ++jb) {
+                const uint4 nx = make_uint4(
+                        pick(wrap, y[jb + 1].x, y[jb].x), pick(wrap, y[jb + 1].y, y[jb].y),
+                        pick(wrap, y[jb + 1].z, y[jb].z), pick(wrap, y[jb + 1].w, y[jb].w));
+                const uint4 o = window16(f.k[h][jb], nx, lo.kr[h]);
+                const uint4 mk = lo.kmask[jb];
+                const uint4 a = make_uint4(o.x & mk.x, o.y & mk.y, o.z & mk.z, o.w & mk.w);
+                if (h == 0)
+                    c0 = mfma(a, qB[jb], c0);
+                else
+                    c1 = mfma(a, qB[jb], c1);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int jb = 0; jb < KB; ++jb) {
+            c0 = mfma(k_operand<KB, KAL>(f, lo, 0, jb), qB[jb], c0);
+            c1 = mfma(k_operand<KB, KAL>(f, lo, 1, jb), qB[jb], c1);
+        }
     }
     // c0[r]: token 4*q4 + r of the step, c1[r]: token 16 + 4*q4 + r (nt of
     // the 32 are valid); head g = lane % 16
@@ -288,13 +368,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode_mfma(
     const size_t kt_row = (size_t)Hkv * keep;
     const size_t v_row = (size_t)Hkv * kD;
     // this wave's first rows of kv head kv; the valid bytes of a step starting
-    // at token ts end at the last valid token's row.  Steps advance by a
-    // multiple of 4 bytes, so a K_thin row that is not 4-byte aligned (odd
-    // keep) is off by the same 2 bytes in every step: the descriptor base
-    // starts `delta` bytes below it.
+    // at token ts end at the last valid token's row.  Steps advance by 32 rows
+    // of 2*Hkv*keep bytes, a multiple of 64, so the row's offset from a 16-byte
+    // (KAL 0) or 4-byte (KAL 1) boundary is the same in every step: the
+    // descriptor base starts `delta` bytes below the row, on that boundary
+    // (k_thin itself is 16-byte aligned, so the bytes read below the row and
+    // past the range's end stay within the 16-byte blocks of valid rows).
     const uint16_t* kw = k_thin + ((size_t)b * s_cap + ws) * kt_row + (size_t)kv * keep;
     const uint16_t* vw = v_cache + ((size_t)b * s_cap + ws) * v_row + (size_t)kv * kD;
-    const uint32_t delta = KAL == 1 ? (uint32_t)(reinterpret_cast<uintptr_t>(kw) & 3u) : 0u;
+    const uint32_t delta = KAL == 0 ? (uint32_t)(reinterpret_cast<uintptr_t>(kw) & 15u)
+                           : KAL == 1 ? (uint32_t)(reinterpret_cast<uintptr_t>(kw) & 3u) : 0u;
     const LaneOffsets<KB> lo = lane_offsets<KB>(keep, kt_row, v_row, n16, q4, delta);
     // descriptors of the step starting at token ts: empty once ts >= we (a
     // wave past the length issues only empty loads, which read zeros without
@@ -302,11 +385,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode_mfma(
     auto rsrc_k = [&](int ts) {
         const int nt = min(32, we - ts);
         // a dword reads as zero unless it ends inside the range, so the range
-        // is rounded up to whole dwords (the extra bytes share the last valid
-        // dword and are masked)
+        // is rounded up to whole dwords, or whole 16-byte chunks for KAL 0
+        // (the extra bytes share the last valid dword or chunk and are masked)
+        const uint32_t rnd = KAL == 0 ? 15u : 3u;
         const uint32_t bytes =
-                nt > 0 ? ((uint32_t)(((nt - 1) * kt_row + keep) * 2) + delta + 3u) & ~3u : 0u;
-        return make_rsrc(reinterpret_cast<const char*>(kw + (size_t)(ts - ws) * kt_row) - delta, bytes);
+                nt > 0 ? ((uint32_t)(((nt - 1) * kt_row + keep) * 2) + delta + rnd) & ~rnd : 0u;
+        return make_rsrc(reinterpret_cast<const char*>(kw + (size_t)(ts - ws) * kt_row) - delta,
+                         bytes);
     };
     auto rsrc_v = [&](int ts) {
         const int nt = min(32, we - ts);
@@ -390,7 +475,13 @@ hipError_t launch_kb(int kal, dim3 grid, hipStream_t s, const uint16_t* q, const
     if (kal == 8)
         k_decode_mfma<KB, 8><<<grid, kThreads, 0, s>>>(q, kt, v, lens, idx, s_cap, Hkv, G, keep,
                                                        scale, chunk, nsplit, rec, part);
-    else if (kal == 2)
+    else if (kal == 0) {
+        if constexpr (KB < 4)
+            k_decode_mfma<KB, 0><<<grid, kThreads, 0, s>>>(q, kt, v, lens, idx, s_cap, Hkv, G,
+                                                           keep, scale, chunk, nsplit, rec, part);
+        else
+            return hipErrorInvalidValue;
+    } else if (kal == 2)
         k_decode_mfma<KB, 2><<<grid, kThreads, 0, s>>>(q, kt, v, lens, idx, s_cap, Hkv, G, keep,
                                                        scale, chunk, nsplit, rec, part);
     else
@@ -426,7 +517,7 @@ hipError_t launch_decode_mfma(const think_dims& d, const DecodeGeom& g, const vo
                               const int32_t* kept_idx, int keep, float scale, float* partials,
                               hipStream_t s) {
     const int G = d.n_q_heads / d.n_kv_heads;
-    const int kal = keep % 8 == 0 ? 8 : (keep % 2 == 0 ? 2 : 1);
+    const int kal = keep % 8 == 0 ? 8 : keep <= 96 ? 0 : keep % 2 == 0 ? 2 : 1;
     const int KB = (keep + 31) / 32;
     dim3 grid(g.nsplit, d.n_kv_heads, d.batch);
     auto qp = (const uint16_t*)q;

@@ -151,6 +151,16 @@ EDGE = [
          seq_capacity=1000, keep=1, dtype="bf16"),
     dict(seed=11, lens=[5000, 2500], batch=2, n_q_heads=32, n_kv_heads=4, head_dim=128,
          seq_capacity=5000, keep=96, dtype="bf16", lowrank=32),
+    # rows at every offset from a 16-byte boundary (odd Hkv*keep), one to three
+    # 32-channel blocks; and the widest odd and even rows off dword boundaries
+    dict(seed=12, lens=[1500, 31, 700], batch=3, n_q_heads=10, n_kv_heads=5, head_dim=128,
+         seq_capacity=1500, keep=33, dtype="bf16", lowrank=8),
+    dict(seed=13, lens=[2100], batch=1, n_q_heads=21, n_kv_heads=3, head_dim=128,
+         seq_capacity=2100, keep=90, dtype="bf16", lowrank=8),
+    dict(seed=14, lens=[999, 64], batch=2, n_q_heads=6, n_kv_heads=3, head_dim=128,
+         seq_capacity=1000, keep=101, dtype="bf16", lowrank=8),
+    dict(seed=15, lens=[640], batch=1, n_q_heads=8, n_kv_heads=1, head_dim=128,
+         seq_capacity=640, keep=126, dtype="bf16", lowrank=8),
 ]
 
 
