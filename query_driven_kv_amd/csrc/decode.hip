@@ -128,7 +128,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_partial(
 template <int DT>
 __global__ __launch_bounds__(1024) void k_decode_combine(
         const float* __restrict__ partials, const int32_t* __restrict__ seq_lens, int s_cap,
-        int chunk, int nsplit, int rec, int D, int sg_count, typename Elem<DT>::T* __restrict__ out) {
+        int chunk, bool per_seq_chunk, int nsplit, int rec, int D, int sg_count,
+        typename Elem<DT>::T* __restrict__ out) {
     using E = Elem<DT>;
     constexpr float kNone = -3.402823466e38f;   // finite stand-in for an empty maximum
     const int h = blockIdx.x, b = blockIdx.y, Hq = gridDim.x;
@@ -153,7 +154,8 @@ __global__ __launch_bounds__(1024) void k_decode_combine(
         // the record loads above are issued before the length is waited on
         asm volatile("" : "+s"(len_raw)::"memory");
         const int len = len_raw < 0 ? 0 : (len_raw > s_cap ? s_cap : len_raw);
-        const int ns = (len + chunk - 1) / chunk;
+        const int cb = per_seq_chunk ? seq_chunk(len, chunk, nsplit) : chunk;
+        const int ns = (len + cb - 1) / cb;
         float mv[8], lv[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -254,12 +256,12 @@ hipError_t launch_decode_combine(const think_dims& d, const DecodeGeom& g, const
     const int cthreads = d.head_dim / 4 * sg_count;
     if (d.dtype == THINK_BF16)
         k_decode_combine<THINK_BF16><<<cgrid, cthreads, 0, s>>>(
-            partials, seq_lens, d.seq_capacity, g.chunk, g.nsplit, g.rec, d.head_dim, sg_count,
-            (uint16_t*)out);
+            partials, seq_lens, d.seq_capacity, g.chunk, g.mfma, g.nsplit, g.rec, d.head_dim,
+            sg_count, (uint16_t*)out);
     else
         k_decode_combine<THINK_F32><<<cgrid, cthreads, 0, s>>>(
-            partials, seq_lens, d.seq_capacity, g.chunk, g.nsplit, g.rec, d.head_dim, sg_count,
-            (float*)out);
+            partials, seq_lens, d.seq_capacity, g.chunk, g.mfma, g.nsplit, g.rec, d.head_dim,
+            sg_count, (float*)out);
     return hipGetLastError();
 }
 

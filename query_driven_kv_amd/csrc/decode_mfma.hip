@@ -6,8 +6,11 @@
 //   l_t = scale * sum_j q[b,h,idx_j] * K_thin[b,t,kv,j],  out = softmax(l) . V[b,:,kv,:]
 //
 // Work decomposition.  Workgroup = (token chunk, kv head, b), 4 waves; each
-// wave walks its quarter of the chunk 32 tokens at a time.  The G <= 16 query
-// heads of the group share every K_thin / V byte the wave loads.
+// wave walks its quarter of the chunk 32 tokens at a time.  The chunk size
+// follows the sequence's own length (all nsplit chunks of a sequence carry
+// tokens), so ragged batches and partly filled caches stay balanced.  The
+// G <= 16 query heads of the group share every K_thin / V byte the wave
+// loads.
 //
 // Both products run on v_mfma_f32_16x16x32_bf16 (16x16 output, K = 32):
 //   logits  C[t][g] = sum_j K_thin[t][j] * qS[j][g]
@@ -320,7 +323,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode_mfma(
     const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x;
     const int Hq = Hkv * G;
-    const int t0 = split * chunk;
     const int lane = tid & 63, wave = tid >> 6;
     const int n16 = lane & 15, q4 = lane >> 4;
 
@@ -362,7 +364,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode_mfma(
         qv[r] = __builtin_amdgcn_raw_buffer_load_b16(rsrc_q, off, 0, 0);
     }
 
-    const int tw = chunk / kWaves;
+    const int cb = seq_chunk(len, chunk, nsplit);
+    const int t0 = split * cb;
+    const int tw = cb / kWaves;
     const int ws = t0 + __builtin_amdgcn_readfirstlane(wave) * tw;   // wave-uniform
     const int we = min(ws + tw, len);
     const size_t kt_row = (size_t)Hkv * keep;

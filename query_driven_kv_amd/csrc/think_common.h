@@ -82,6 +82,20 @@ __device__ __forceinline__ int clamp_len(const int32_t* seq_lens, int b, int s_c
     return n < 0 ? 0 : (n > s_cap ? s_cap : n);
 }
 
+// Tokens per chunk of one sequence in the matrix-core decode: a sequence's
+// `len` tokens are spread over all `nsplit` chunk slots in whole 128-token
+// units (4 waves x one 32-token step), at least 512 and at most `cap_chunk`
+// (the chunk at full capacity), so a sequence shorter than the capacity still
+// keeps every one of its workgroups streaming.  The chunk pass and the
+// combine both derive the chunk from the length this way, so they agree on
+// which slots hold records.
+__device__ __forceinline__ int seq_chunk(int len, int cap_chunk, int nsplit) {
+    int c = (int)(((unsigned)len + (unsigned)nsplit - 1u) / (unsigned)nsplit);
+    c = (c + 127) & ~127;
+    c = c < 512 ? 512 : c;
+    return c > cap_chunk ? cap_chunk : c;
+}
+
 inline int elem_bytes(int dtype) { return dtype == THINK_F32 ? 4 : 2; }
 
 // ---------------------------------------------------------------------------
@@ -98,7 +112,7 @@ struct ScoreGeom {
 ScoreGeom score_geom(const think_dims& d);
 
 struct DecodeGeom {
-    int chunk;        // tokens per workgroup
+    int chunk;        // tokens per workgroup (matrix-core kernel: at full capacity)
     int nsplit;       // splits per sequence
     int rec;          // floats per partial record: m, l, 2 pad, o[D]
     bool mfma;        // bf16 matrix-core kernel

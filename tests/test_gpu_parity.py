@@ -161,6 +161,9 @@ EDGE = [
          seq_capacity=1000, keep=101, dtype="bf16", lowrank=8),
     dict(seed=15, lens=[640], batch=1, n_q_heads=8, n_kv_heads=1, head_dim=128,
          seq_capacity=640, keep=126, dtype="bf16", lowrank=8),
+    # a cache filled far below its capacity: the chunk follows the length
+    dict(seed=16, lens=[3000, 11], batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128,
+         seq_capacity=20000, keep=64, dtype="bf16", lowrank=8),
 ]
 
 
