@@ -121,25 +121,39 @@ __global__ __launch_bounds__(kThreads) void k_decode_partial(
 // sub-group sg merges a contiguous range of the nsplit chunk slots in
 // ascending order, eight at a time with a running maximum, then the SG results
 // are merged in ascending sg order.  Fixed order, so the result is bitwise
-// reproducible.  The ranges are fixed by nsplit rather than by the length, so
-// the record loads do not wait for the length load; slots at or past the
-// sequence's chunk count are dropped after loading (their contents are never
-// used).
+// reproducible.  Fixed and per-sequence chunks: the ranges are fixed by nsplit
+// rather than by the length, so the record loads do not wait for the length
+// load; slots at or past the sequence's chunk count are dropped after loading
+// (their contents are never used).  Balanced slots: every wave first derives
+// the sequence's slot range from all B lengths (balanced_slots), then loads.
 template <int DT>
 __global__ __launch_bounds__(1024) void k_decode_combine(
         const float* __restrict__ partials, const int32_t* __restrict__ seq_lens, int s_cap,
-        int chunk, bool per_seq_chunk, int nsplit, int rec, int D, int sg_count,
+        int chunk, int mode, int nsplit, int rec, int D, int sg_count,
         typename Elem<DT>::T* __restrict__ out) {
     using E = Elem<DT>;
     constexpr float kNone = -3.402823466e38f;   // finite stand-in for an empty maximum
-    const int h = blockIdx.x, b = blockIdx.y, Hq = gridDim.x;
+    const int h = blockIdx.x, b = blockIdx.y, Hq = gridDim.x, nb = gridDim.y;
     const int tid = threadIdx.x;
     const int D4 = D >> 2;
     const int d4 = tid % D4, sg = tid / D4;
     const float* base = partials + ((size_t)b * Hq + h) * nsplit * rec;
-    const int lo = (int)((unsigned)(sg * nsplit) / (unsigned)sg_count);
-    const int hi = (int)((unsigned)((sg + 1) * nsplit) / (unsigned)sg_count);
-    int len_raw = seq_lens[b];
+    int nrange = nsplit, used = 0;               // slots in the ranges; used: balanced only
+    int len_raw = 0;
+    if (mode == kBalanced) {
+        const int lane = tid & 63;   // lanes past B read zero
+        const int lr = __builtin_amdgcn_raw_buffer_load_b32(
+                make_rsrc(seq_lens, (uint32_t)nb * 4u), lane * 4, 0, 0);
+        const SeqSlots ss = balanced_slots(lr < 0 ? 0 : (lr > s_cap ? s_cap : lr), nsplit * nb);
+        const int first = __builtin_amdgcn_readfirstlane(__shfl(ss.first, b));
+        used = __builtin_amdgcn_readfirstlane(__shfl(ss.used, b));
+        base = partials + ((size_t)h * nsplit * nb + first) * rec;
+        nrange = used;
+    } else {
+        len_raw = seq_lens[b];
+    }
+    const int lo = (int)((unsigned)(sg * nrange) / (unsigned)sg_count);
+    const int hi = (int)((unsigned)((sg + 1) * nrange) / (unsigned)sg_count);
     float M = kNone, L = 0.0f;
     float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s0 = lo; s0 < hi; s0 += 8) {
@@ -147,15 +161,15 @@ __global__ __launch_bounds__(1024) void k_decode_combine(
         float4 ov[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            const float* r = base + (size_t)min(s0 + k, nsplit - 1) * rec;
+            const float* r = base + (size_t)min(s0 + k, nrange - 1) * rec;
             ml[k] = *reinterpret_cast<const float2*>(r);
             ov[k] = *reinterpret_cast<const float4*>(r + 4 + 4 * d4);
         }
         // the record loads above are issued before the length is waited on
         asm volatile("" : "+s"(len_raw)::"memory");
         const int len = len_raw < 0 ? 0 : (len_raw > s_cap ? s_cap : len_raw);
-        const int cb = per_seq_chunk ? seq_chunk(len, chunk, nsplit) : chunk;
-        const int ns = (len + cb - 1) / cb;
+        const int cb = mode == kSeqChunk ? seq_chunk(len, chunk, nsplit) : chunk;
+        const int ns = mode == kBalanced ? used : (len + cb - 1) / cb;
         float mv[8], lv[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -220,6 +234,7 @@ __global__ __launch_bounds__(1024) void k_decode_combine(
 DecodeGeom decode_geom(const think_dims& d, int keep) {
     DecodeGeom g{};
     g.mfma = mfma_decode_supported(d, keep);
+    g.mode = !g.mfma ? kFixedChunk : (d.batch >= 2 && d.batch <= 64 ? kBalanced : kSeqChunk);
     g.chunk = g.mfma ? mfma_decode_chunk(d, keep) : kChunk;
     g.nsplit = (d.seq_capacity + g.chunk - 1) / g.chunk;
     g.rec = d.head_dim + 4;
@@ -256,11 +271,11 @@ hipError_t launch_decode_combine(const think_dims& d, const DecodeGeom& g, const
     const int cthreads = d.head_dim / 4 * sg_count;
     if (d.dtype == THINK_BF16)
         k_decode_combine<THINK_BF16><<<cgrid, cthreads, 0, s>>>(
-            partials, seq_lens, d.seq_capacity, g.chunk, g.mfma, g.nsplit, g.rec, d.head_dim,
+            partials, seq_lens, d.seq_capacity, g.chunk, g.mode, g.nsplit, g.rec, d.head_dim,
             sg_count, (uint16_t*)out);
     else
         k_decode_combine<THINK_F32><<<cgrid, cthreads, 0, s>>>(
-            partials, seq_lens, d.seq_capacity, g.chunk, g.mfma, g.nsplit, g.rec, d.head_dim,
+            partials, seq_lens, d.seq_capacity, g.chunk, g.mode, g.nsplit, g.rec, d.head_dim,
             sg_count, (float*)out);
     return hipGetLastError();
 }

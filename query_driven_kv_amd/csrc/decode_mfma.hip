@@ -37,6 +37,8 @@
 // valid token: padding tokens (t >= len_b) read as zero and their logits are
 // set to -inf, so a NaN in padding cannot leak in; no load sits behind a
 // branch.
+#include <type_traits>
+
 #include "think_common.h"
 
 namespace thinkkv {
@@ -216,8 +218,10 @@ __device__ __forceinline__ uint4 window16(const uint4& lo, const uint4& hi, uint
                    u3 = pick(s8, hi.y, lo.w), u4 = pick(s8, hi.z, hi.x), u5 = pick(s8, hi.w, hi.y);
     const uint32_t a0 = pick(s4, u1, u0), a1 = pick(s4, u2, u1), a2 = pick(s4, u3, u2),
                    a3 = pick(s4, u4, u3), a4 = pick(s4, u5, u4);
-    return make_uint4(__builtin_amdgcn_alignbyte(a1, a0, rb), __builtin_amdgcn_alignbyte(a2, a1, rb),
-                      __builtin_amdgcn_alignbyte(a3, a2, rb), __builtin_amdgcn_alignbyte(a4, a3, rb));
+    return make_uint4(__builtin_amdgcn_alignbyte(a1, a0, rb),
+                      __builtin_amdgcn_alignbyte(a2, a1, rb),
+                      __builtin_amdgcn_alignbyte(a3, a2, rb),
+                      __builtin_amdgcn_alignbyte(a4, a3, rb));
 }
 
 // x of the lane 16 above (wrapping within the wave).
@@ -319,8 +323,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode_mfma(
         const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_thin,
         const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ seq_lens,
         const int32_t* __restrict__ kept_idx, int s_cap, int Hkv, int G, int keep, float scale,
-        int chunk, int nsplit, int rec, float* __restrict__ partials) {
-    const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+        int chunk, int nsplit, int rec, int mode, float* __restrict__ partials) {
+    const int split = blockIdx.x, kv = blockIdx.y;
     const int tid = threadIdx.x;
     const int Hq = Hkv * G;
     const int lane = tid & 63, wave = tid >> 6;
@@ -336,24 +340,63 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode_mfma(
     // K_thin/V fragments are issued back to back, and only then does the
     // workgroup wait for the query to build the MFMA operand.
     constexpr int kGather = 16 * KB * 32 / kThreads;
-    const int len_raw = seq_lens[b];
+    // Balanced slots (2 <= B <= 64): this workgroup is chunk slot
+    // split + nsplit * blockIdx.z of its kv head; every wave reads the B
+    // lengths (a bounded buffer load: lanes past B read zero) and finds the
+    // sequence that owns the slot and its token range.  The kept indices of
+    // sequence blockIdx.z are loaded meanwhile, as a guess that holds for all
+    // but the slots near a share boundary; a wrong guess loads them again.
+    // A slot no sequence fills exits, uniformly for the workgroup.
+    // Otherwise the workgroup is chunk `split` of sequence blockIdx.z.
+    //
     // The gather reads through buffer descriptors bounded to this kv head's
     // kept indices and its G query rows: slots past keep or past G read zero
     // in hardware, so every load is unconditional and none waits on another.
     // A chunk that starts past the length still runs (all its stream loads
     // are empty) and writes a record the combine never reads; an early exit
     // here would put the length load in front of the gather.
-    const auto rsrc_idx = make_rsrc(kept_idx + ((size_t)b * Hkv + kv) * keep, (uint32_t)keep * 4u);
-    const auto rsrc_q = make_rsrc(q + ((size_t)b * Hq + (size_t)kv * G) * kD, (uint32_t)(G * kD * 2));
+    const int nb = gridDim.z, slot = split + nsplit * (int)blockIdx.z;
+    int b = blockIdx.z, len_raw = 0, lr = 0, len = 0, cb = 0, t0 = 0;
+    if (mode == kBalanced)
+        lr = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(seq_lens, (uint32_t)nb * 4u), lane * 4,
+                                                  0, 0);
+    else
+        len_raw = seq_lens[b];
     int cidx[kGather];
+    auto load_idx = [&](int bb) {
+        const auto rsrc_idx =
+                make_rsrc(kept_idx + ((size_t)bb * Hkv + kv) * keep, (uint32_t)keep * 4u);
 #pragma unroll
-    for (int r = 0; r < kGather; ++r) {
-        const int j = (tid + r * kThreads) % (KB * 32);
-        cidx[r] = __builtin_amdgcn_raw_buffer_load_b32(rsrc_idx, j * 4, 0, 0);
-    }
+        for (int r = 0; r < kGather; ++r) {
+            const int j = (tid + r * kThreads) % (KB * 32);
+            cidx[r] = __builtin_amdgcn_raw_buffer_load_b32(rsrc_idx, j * 4, 0, 0);
+        }
+    };
+    load_idx(b);
     // both loads are in flight before either is waited on
-    asm volatile("" ::"s"(len_raw), "v"(cidx[0]));
-    const int len = len_raw < 0 ? 0 : (len_raw > s_cap ? s_cap : len_raw);
+    asm volatile("" ::"s"(len_raw), "v"(lr), "v"(cidx[0]));
+    if (mode == kBalanced) {
+        const int li = lr < 0 ? 0 : (lr > s_cap ? s_cap : lr);
+        const SeqSlots ss = balanced_slots(li, nsplit * nb);
+        const unsigned long long own = __ballot(ss.n > 0 && slot < ss.first + ss.n);
+        if (own == 0) return;
+        const int owner = __builtin_amdgcn_readfirstlane(__ffsll((long long)own) - 1);
+        const int j = slot - __builtin_amdgcn_readfirstlane(__shfl(ss.first, owner));
+        if (j >= __builtin_amdgcn_readfirstlane(__shfl(ss.used, owner))) return;
+        len = __builtin_amdgcn_readfirstlane(__shfl(li, owner));
+        cb = __builtin_amdgcn_readfirstlane(__shfl(ss.chunk, owner));
+        t0 = j * cb;
+        if (owner != b) {
+            b = owner;
+            load_idx(b);
+        }
+    } else {
+        len = len_raw < 0 ? 0 : (len_raw > s_cap ? s_cap : len_raw);
+        cb = seq_chunk(len, chunk, nsplit);
+        t0 = split * cb;
+    }
+    const auto rsrc_q =
+            make_rsrc(q + ((size_t)b * Hq + (size_t)kv * G) * kD, (uint32_t)(G * kD * 2));
     uint16_t qv[kGather];
 #pragma unroll
     for (int r = 0; r < kGather; ++r) {
@@ -364,8 +407,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode_mfma(
         qv[r] = __builtin_amdgcn_raw_buffer_load_b16(rsrc_q, off, 0, 0);
     }
 
-    const int cb = seq_chunk(len, chunk, nsplit);
-    const int t0 = split * cb;
     const int tw = cb / kWaves;
     const int ws = t0 + __builtin_amdgcn_readfirstlane(wave) * tw;   // wave-uniform
     const int we = min(ws + tw, len);
@@ -461,7 +502,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode_mfma(
             L = fmaf(f, s_l[w * 16 + g], L);
             o = fmaf(f, s_o[(w * 16 + g) * kD + d], o);
         }
-        float* r = partials + (((size_t)b * Hq + kv * G + g) * nsplit + split) * rec;
+        float* r = partials + (mode == kBalanced
+                                       ? ((size_t)(kv * G + g) * nsplit * nb + slot) * rec
+                                       : (((size_t)b * Hq + kv * G + g) * nsplit + split) * rec);
         r[4 + d] = o;
         if (d == 0) {
             r[0] = M;
@@ -475,22 +518,23 @@ template <int KB>
 hipError_t launch_kb(int kal, dim3 grid, hipStream_t s, const uint16_t* q, const uint16_t* kt,
                      const uint16_t* v, const int32_t* lens, const int32_t* idx, int s_cap,
                      int Hkv, int G, int keep, float scale, int chunk, int nsplit, int rec,
-                     float* part) {
+                     int mode, float* part) {
     if (kal == 8)
         k_decode_mfma<KB, 8><<<grid, kThreads, 0, s>>>(q, kt, v, lens, idx, s_cap, Hkv, G, keep,
-                                                       scale, chunk, nsplit, rec, part);
+                                                       scale, chunk, nsplit, rec, mode, part);
     else if (kal == 0) {
         if constexpr (KB < 4)
             k_decode_mfma<KB, 0><<<grid, kThreads, 0, s>>>(q, kt, v, lens, idx, s_cap, Hkv, G,
-                                                           keep, scale, chunk, nsplit, rec, part);
+                                                           keep, scale, chunk, nsplit, rec, mode,
+                                                           part);
         else
             return hipErrorInvalidValue;
     } else if (kal == 2)
         k_decode_mfma<KB, 2><<<grid, kThreads, 0, s>>>(q, kt, v, lens, idx, s_cap, Hkv, G, keep,
-                                                       scale, chunk, nsplit, rec, part);
+                                                       scale, chunk, nsplit, rec, mode, part);
     else
         k_decode_mfma<KB, 1><<<grid, kThreads, 0, s>>>(q, kt, v, lens, idx, s_cap, Hkv, G, keep,
-                                                       scale, chunk, nsplit, rec, part);
+                                                       scale, chunk, nsplit, rec, mode, part);
     return hipGetLastError();
 }
 
@@ -527,15 +571,16 @@ hipError_t launch_decode_mfma(const think_dims& d, const DecodeGeom& g, const vo
     auto qp = (const uint16_t*)q;
     auto kp = (const uint16_t*)k_thin;
     auto vp = (const uint16_t*)v_cache;
+    auto go = [&](auto kb) {
+        return launch_kb<decltype(kb)::value>(kal, grid, s, qp, kp, vp, seq_lens, kept_idx,
+                                              d.seq_capacity, d.n_kv_heads, G, keep, scale,
+                                              g.chunk, g.nsplit, g.rec, g.mode, partials);
+    };
     switch (KB) {
-        case 1: return launch_kb<1>(kal, grid, s, qp, kp, vp, seq_lens, kept_idx, d.seq_capacity,
-                                    d.n_kv_heads, G, keep, scale, g.chunk, g.nsplit, g.rec, partials);
-        case 2: return launch_kb<2>(kal, grid, s, qp, kp, vp, seq_lens, kept_idx, d.seq_capacity,
-                                    d.n_kv_heads, G, keep, scale, g.chunk, g.nsplit, g.rec, partials);
-        case 3: return launch_kb<3>(kal, grid, s, qp, kp, vp, seq_lens, kept_idx, d.seq_capacity,
-                                    d.n_kv_heads, G, keep, scale, g.chunk, g.nsplit, g.rec, partials);
-        default: return launch_kb<4>(kal, grid, s, qp, kp, vp, seq_lens, kept_idx, d.seq_capacity,
-                                     d.n_kv_heads, G, keep, scale, g.chunk, g.nsplit, g.rec, partials);
+        case 1: return go(std::integral_constant<int, 1>{});
+        case 2: return go(std::integral_constant<int, 2>{});
+        case 3: return go(std::integral_constant<int, 3>{});
+        default: return go(std::integral_constant<int, 4>{});
     }
 }
 

@@ -96,6 +96,60 @@ __device__ __forceinline__ int seq_chunk(int len, int cap_chunk, int nsplit) {
     return c > cap_chunk ? cap_chunk : c;
 }
 
+// Chunk slots of a batch of 2..64 sequences, shared in proportion to length.
+// The batch's nslots = B * nsplit slots per kv head are dealt so that every
+// non-empty sequence gets one slot plus its share of the rest by length
+// (boundaries floor(M * prefix / total), M = nslots - non-empty count, so the
+// counts add up to nslots exactly), and its chunk is its length over its slot
+// count in whole 128-token units (at least 512).  Every slot then carries
+// about the same number of tokens however ragged the batch is.  Called by all
+// 64 lanes of a wave; lane i < B passes sequence i's clamped length (0 past
+// B) and gets sequence i's slot count, first slot, chunk and used slots.
+// The chunk pass and the combine both compute this, so they agree.
+struct SeqSlots {
+    int n;       // slots dealt to the sequence
+    int first;   // its first slot
+    int chunk;   // tokens per slot
+    int used;    // slots that hold tokens: ceil(len / chunk) <= n
+};
+__device__ __forceinline__ SeqSlots balanced_slots(int len, int nslots) {
+    const int lane = threadIdx.x & 63;
+    const int nonempty = __popcll(__ballot(len > 0));
+    long long inc = len;                          // inclusive prefix of the lengths
+    for (int o = 1; o < 64; o <<= 1) {
+        const long long y = __shfl_up(inc, o);
+        if (lane >= o) inc += y;
+    }
+    const long long total = __shfl(inc, 63);
+    SeqSlots r{0, 0, 512, 0};
+    if (len > 0) {
+        // M * prefix < 2^48 and total < 2^35: the quotients are exact to well
+        // within 1/total, so the floors are those of the integer division
+        const double M = (double)(nslots - nonempty), T = (double)total;
+        r.n = 1 + (int)floor(M * (double)inc / T) - (int)floor(M * (double)(inc - len) / T);
+    }
+    int ninc = r.n;                               // inclusive prefix of the slot counts
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(ninc, o);
+        if (lane >= o) ninc += y;
+    }
+    r.first = ninc - r.n;
+    if (r.n > 0) {
+        int c = (len + r.n - 1) / r.n;
+        c = (c + 127) & ~127;
+        r.chunk = c < 512 ? 512 : c;
+        r.used = (len + r.chunk - 1) / r.chunk;
+    }
+    return r;
+}
+
+// How the decode's chunk slots are laid out (DecodeGeom::mode).
+enum DecodeMode {
+    kFixedChunk = 0,   // general kernel: fixed chunk, records [B][Hq][nsplit]
+    kSeqChunk = 1,     // matrix-core kernel: per-sequence chunk (seq_chunk), same records
+    kBalanced = 2      // matrix-core kernel, 2 <= B <= 64: balanced_slots, records [Hq][B*nsplit]
+};
+
 inline int elem_bytes(int dtype) { return dtype == THINK_F32 ? 4 : 2; }
 
 // ---------------------------------------------------------------------------
@@ -116,7 +170,8 @@ struct DecodeGeom {
     int nsplit;       // splits per sequence
     int rec;          // floats per partial record: m, l, 2 pad, o[D]
     bool mfma;        // bf16 matrix-core kernel
-    size_t ws_bytes;  // records [B][Hq][nsplit][rec] fp32
+    int mode;         // DecodeMode
+    size_t ws_bytes;  // B * Hq * nsplit records of rec fp32
 };
 DecodeGeom decode_geom(const think_dims& d, int keep);
 

@@ -164,6 +164,13 @@ EDGE = [
     # a cache filled far below its capacity: the chunk follows the length
     dict(seed=16, lens=[3000, 11], batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128,
          seq_capacity=20000, keep=64, dtype="bf16", lowrank=8),
+    # 64 ragged sequences (chunk slots dealt by length), and 65 (past the batch
+    # size that deals slots: per-sequence chunks)
+    dict(seed=17, lens=[(i * 37) % 700 + 1 for i in range(64)], batch=64,
+         n_q_heads=8, n_kv_heads=2, head_dim=128, seq_capacity=700, keep=51, dtype="bf16",
+         lowrank=8),
+    dict(seed=18, lens=[(i * 53) % 600 + 1 for i in range(65)], batch=65, n_q_heads=4,
+         n_kv_heads=1, head_dim=128, seq_capacity=600, keep=64, dtype="bf16", lowrank=8),
 ]
 
 
@@ -198,6 +205,32 @@ def test_exact_tie_goes_to_lower_channel_and_is_flagged():
     assert g["tie"][0, 0] == 1
     kept = set(g["idx"][0, 0].tolist())
     assert a in kept and b not in kept
+
+
+def test_empty_sequences_in_a_ragged_batch_decode_to_zero():
+    """Matrix-core decode with chunk slots dealt by length: empty sequences
+    get no slot and a zero output; the others match the oracle one by one."""
+    qdk = _qdk()
+    lens = np.array([0, 900, 0, 5, 1300, 0, 1, 640, 0, 0, 77, 1024], np.int32)
+    B, Hq, Hkv, D, S, keep = len(lens), 8, 2, 128, 1300, 51
+    rng = np.random.default_rng(23)
+    bf = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16)
+    q = bf(rng.standard_normal((B, Hq, D)))
+    thin = bf(rng.standard_normal((B, S, Hkv, keep)))
+    v = bf(rng.standard_normal((B, S, Hkv, D)))
+    idx = np.sort(np.stack([np.stack([rng.choice(D, keep, replace=False) for _ in range(Hkv)])
+                            for _ in range(B)]), axis=-1).astype(np.int32)
+    out = qdk.think_decode_attn(q.cuda(), thin.cuda(), v.cuda(), to_dev(lens), to_dev(idx), 0.1)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    h = lambda t: t.view(torch.int16).numpy().view(np.uint16)
+    for b in range(B):
+        if lens[b] == 0:
+            assert (got[b] == 0).all(), b
+            continue
+        ref = oracle.decode(h(q[b:b + 1]), h(thin[b:b + 1]), h(v[b:b + 1]), lens[b:b + 1],
+                            idx[b:b + 1], np.float32(0.1))
+        assert row_rel_err(out[b:b + 1], ref).max() <= 2e-2, b
 
 
 def test_zero_length_sequence_gives_zero_scores_and_output():
