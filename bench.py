@@ -170,19 +170,23 @@ class Workload:
                 self.dc_i += 1
                 yield self.dec_args[c][s][l]
 
-    def decode_kernel_times(self, stream, torch):
-        """One step's decode calls in split-phase form, with HIP events on the
-        launch stream around every chunk-pass launch: the chunk pass's mean
-        launch duration in microseconds."""
+    def decode_kernel_times(self, stream, torch, min_launches=64):
+        """One step's decode calls (repeated until at least `min_launches`) in
+        split-phase form, with HIP events on the launch stream around every
+        chunk-pass launch: the chunk pass's mean launch duration in
+        microseconds, the launch count and the 10/50/90th percentiles."""
         from query_driven_kv_amd import _lib
         lib, P = _lib.lib, ctypes.c_void_p
         d, keep = ctypes.byref(self.dims), self.cfg.keep
         out, ws, wsn = P(self.out.data_ptr()), P(self.ws_d.data_ptr()), self.ws_d.numel()
-        n = self.cfg.decode_steps * self.cfg.layers
+        per_step = self.cfg.decode_steps * self.cfg.layers
+        passes = max(1, -(-min_launches // per_step))
+        n = passes * per_step
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(n)]
+        calls = [c for _ in range(passes) for c in self.decode_calls()]
         k = 0
-        for (q, thin, v, lens, idx) in self.decode_calls():
+        for (q, thin, v, lens, idx) in calls:
             ev[k][0].record()
             _lib.check("think_decode_attn_partial", lib.think_decode_attn_partial(
                 d, q, thin, v, lens, idx, keep, self.scale, ws, wsn, stream))
@@ -515,8 +519,9 @@ def main():
                      "algorithmic_bytes_per_launch": bm["dec_call"],
                      "launch_us": round(part_us, 2) if n_part else None,
                      "launch_us_p10_p50_p90": part_pct,
-                     "timing": (f"HIP events on the launch stream around each of the {n_part} "
-                                f"chunk-pass launches of one step, after the timed steps"),
+                     "timing": (f"HIP events on the launch stream around each of {n_part} "
+                                f"chunk-pass launches (one step's decode calls, repeated to at "
+                                f"least 64), after the timed steps"),
                      "traffic_source": traffic_src},
         "near_ties": near,
         "input_copies": wl.ncopies,

@@ -144,7 +144,8 @@ __global__ __launch_bounds__(1024) void k_decode_combine(
         const int lane = tid & 63;   // lanes past B read zero
         const int lr = __builtin_amdgcn_raw_buffer_load_b32(
                 make_rsrc(seq_lens, (uint32_t)nb * 4u), lane * 4, 0, 0);
-        const SeqSlots ss = balanced_slots(lr < 0 ? 0 : (lr > s_cap ? s_cap : lr), nsplit * nb);
+        const SeqSlots ss = balanced_slots(lr < 0 ? 0 : (lr > s_cap ? s_cap : lr), nsplit * nb,
+                                           kDecodeUnit, kDecodeMinChunk);
         const int first = __builtin_amdgcn_readfirstlane(__shfl(ss.first, b));
         used = __builtin_amdgcn_readfirstlane(__shfl(ss.used, b));
         base = partials + ((size_t)h * nsplit * nb + first) * rec;

@@ -377,7 +377,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode_mfma(
     asm volatile("" ::"s"(len_raw), "v"(lr), "v"(cidx[0]));
     if (mode == kBalanced) {
         const int li = lr < 0 ? 0 : (lr > s_cap ? s_cap : lr);
-        const SeqSlots ss = balanced_slots(li, nsplit * nb);
+        const SeqSlots ss = balanced_slots(li, nsplit * nb, kDecodeUnit, kDecodeMinChunk);
         const unsigned long long own = __ballot(ss.n > 0 && slot < ss.first + ss.n);
         if (own == 0) return;
         const int owner = __builtin_amdgcn_readfirstlane(__ffsll((long long)own) - 1);

@@ -89,30 +89,32 @@ __device__ __forceinline__ int clamp_len(const int32_t* seq_lens, int b, int s_c
 // keeps every one of its workgroups streaming.  The chunk pass and the
 // combine both derive the chunk from the length this way, so they agree on
 // which slots hold records.
+constexpr int kDecodeUnit = 128, kDecodeMinChunk = 512;
 __device__ __forceinline__ int seq_chunk(int len, int cap_chunk, int nsplit) {
     int c = (int)(((unsigned)len + (unsigned)nsplit - 1u) / (unsigned)nsplit);
-    c = (c + 127) & ~127;
-    c = c < 512 ? 512 : c;
+    c = (c + kDecodeUnit - 1) & ~(kDecodeUnit - 1);
+    c = c < kDecodeMinChunk ? kDecodeMinChunk : c;
     return c > cap_chunk ? cap_chunk : c;
 }
 
-// Chunk slots of a batch of 2..64 sequences, shared in proportion to length.
-// The batch's nslots = B * nsplit slots per kv head are dealt so that every
+// Token-range slots of a batch of 2..64 sequences, shared in proportion to
+// length.  The batch's nslots = B * nsplit slots are dealt so that every
 // non-empty sequence gets one slot plus its share of the rest by length
 // (boundaries floor(M * prefix / total), M = nslots - non-empty count, so the
 // counts add up to nslots exactly), and its chunk is its length over its slot
-// count in whole 128-token units (at least 512).  Every slot then carries
-// about the same number of tokens however ragged the batch is.  Called by all
-// 64 lanes of a wave; lane i < B passes sequence i's clamped length (0 past
-// B) and gets sequence i's slot count, first slot, chunk and used slots.
-// The chunk pass and the combine both compute this, so they agree.
+// count in whole `unit`-token units (at least `min_chunk`; both powers of
+// two).  Every slot then carries about the same number of tokens however
+// ragged the batch is.  Called by all 64 lanes of a wave; lane i < B passes
+// sequence i's clamped length (0 past B) and gets sequence i's slot count,
+// first slot, chunk and used slots.  The kernel that fills the slots and the
+// one that reads them both compute this, so they agree.
 struct SeqSlots {
     int n;       // slots dealt to the sequence
     int first;   // its first slot
     int chunk;   // tokens per slot
     int used;    // slots that hold tokens: ceil(len / chunk) <= n
 };
-__device__ __forceinline__ SeqSlots balanced_slots(int len, int nslots) {
+__device__ __forceinline__ SeqSlots balanced_slots(int len, int nslots, int unit, int min_chunk) {
     const int lane = threadIdx.x & 63;
     const int nonempty = __popcll(__ballot(len > 0));
     long long inc = len;                          // inclusive prefix of the lengths
@@ -121,7 +123,7 @@ __device__ __forceinline__ SeqSlots balanced_slots(int len, int nslots) {
         if (lane >= o) inc += y;
     }
     const long long total = __shfl(inc, 63);
-    SeqSlots r{0, 0, 512, 0};
+    SeqSlots r{0, 0, min_chunk, 0};
     if (len > 0) {
         // M * prefix < 2^48 and total < 2^35: the quotients are exact to well
         // within 1/total, so the floors are those of the integer division
@@ -136,8 +138,8 @@ __device__ __forceinline__ SeqSlots balanced_slots(int len, int nslots) {
     r.first = ninc - r.n;
     if (r.n > 0) {
         int c = (len + r.n - 1) / r.n;
-        c = (c + 127) & ~127;
-        r.chunk = c < 512 ? 512 : c;
+        c = (c + unit - 1) & ~(unit - 1);
+        r.chunk = c < min_chunk ? min_chunk : c;
         r.used = (len + r.chunk - 1) / r.chunk;
     }
     return r;
