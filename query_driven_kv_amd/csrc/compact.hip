@@ -38,15 +38,27 @@ __global__ __launch_bounds__(kThreads) void k_compact(
     uint16_t* srcmap = reinterpret_cast<uint16_t*>(rows + (size_t)tile * R);
     const int tid = threadIdx.x;
 
+    const int nvec = nt * R * (int)sizeof(E) / 16;
+    const uint4* src = reinterpret_cast<const uint4*>(k_cache + ((size_t)b * s_cap + t0) * R);
+    // The first four row vectors per thread (16 KiB per workgroup, the whole
+    // tile for 2 KiB rows) are loaded into registers first, through a
+    // descriptor bounded to the tile (vectors past it read zero), so they are
+    // in flight together with the kept-index loads of the source map: one
+    // memory round trip instead of two.  Larger tiles load the rest after.
+    const auto rsrc = make_rsrc(src, (uint32_t)nvec * 16u);
+    uint4 first[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) first[k] = ldb_stream(rsrc, (uint32_t)(tid + k * kThreads) * 16u);
     for (int o = tid; o < Ro; o += kThreads) {
         const int kv = o / keep, j = o - kv * keep;
         int c = kept_idx[((size_t)b * Hkv + kv) * keep + j];
         c = c < 0 ? 0 : (c >= D ? D - 1 : c);
         srcmap[o] = (uint16_t)(kv * D + c);
     }
-    const int nvec = nt * R * (int)sizeof(E) / 16;
-    const uint4* src = reinterpret_cast<const uint4*>(k_cache + ((size_t)b * s_cap + t0) * R);
-    for (int v = tid; v < nvec; v += kThreads) lds[v] = ldg_stream(src + v);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        if (tid + k * kThreads < nvec) lds[tid + k * kThreads] = first[k];
+    for (int v = tid + 4 * kThreads; v < nvec; v += kThreads) lds[v] = ldg_stream(src + v);
     __syncthreads();
 
     const size_t E0 = ((size_t)b * s_cap + t0) * Ro;
