@@ -40,15 +40,18 @@ __global__ __launch_bounds__(kThreads) void k_compact(
 
     const int nvec = nt * R * (int)sizeof(E) / 16;
     const uint4* src = reinterpret_cast<const uint4*>(k_cache + ((size_t)b * s_cap + t0) * R);
-    // The first four row vectors per thread (16 KiB per workgroup, the whole
-    // tile for 2 KiB rows) are loaded into registers first, through a
-    // descriptor bounded to the tile (vectors past it read zero), so they are
-    // in flight together with the kept-index loads of the source map: one
-    // memory round trip instead of two.  Larger tiles load the rest after.
+    // The first kFirst row vectors per thread (32 KiB per workgroup: every
+    // tile of up to 32 KiB) are loaded into registers first, through a
+    // descriptor bounded to the tile (vectors past it read zero without
+    // touching memory), so they are in flight together with the kept-index
+    // loads of the source map: one memory round trip instead of two.  Larger
+    // tiles load the rest after.
+    constexpr int kFirst = 8;
     const auto rsrc = make_rsrc(src, (uint32_t)nvec * 16u);
-    uint4 first[4];
+    uint4 first[kFirst];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) first[k] = ldb_stream(rsrc, (uint32_t)(tid + k * kThreads) * 16u);
+    for (int k = 0; k < kFirst; ++k)
+        first[k] = ldb_stream(rsrc, (uint32_t)(tid + k * kThreads) * 16u);
     for (int o = tid; o < Ro; o += kThreads) {
         const int kv = o / keep, j = o - kv * keep;
         int c = kept_idx[((size_t)b * Hkv + kv) * keep + j];
@@ -56,9 +59,9 @@ __global__ __launch_bounds__(kThreads) void k_compact(
         srcmap[o] = (uint16_t)(kv * D + c);
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+    for (int k = 0; k < kFirst; ++k)
         if (tid + k * kThreads < nvec) lds[tid + k * kThreads] = first[k];
-    for (int v = tid + 4 * kThreads; v < nvec; v += kThreads) lds[v] = ldg_stream(src + v);
+    for (int v = tid + kFirst * kThreads; v < nvec; v += kThreads) lds[v] = ldg_stream(src + v);
     __syncthreads();
 
     const size_t E0 = ((size_t)b * s_cap + t0) * Ro;
