@@ -163,6 +163,7 @@ struct ScoreGeom {
     int ncg;           // column groups of <= 256 vectors
     int tpw;           // tokens per workgroup
     int nsplit;        // token splits per sequence
+    bool keep_in_llc;  // read K with plain loads (it fits the last-level cache)
     size_t ws_bytes;   // fp32 partials [B][nsplit][Hkv*D]
 };
 ScoreGeom score_geom(const think_dims& d);
