@@ -85,124 +85,90 @@ __device__ __forceinline__ uint4 v_column(const uint4 (&v)[8]) {
     return r;
 }
 
-// K_thin octets (8 channels, 16 bytes of one head row).  KAL = 8: head rows
-// are 16-byte aligned and an octet is one aligned dwordx4.  KAL = 0 (keep not
-// a multiple of 8, at most 96): each lane loads the 16-byte aligned chunks
-// 4*jb + q4 of its token row (lanes q4 = 0 one more, chunk 4*KB); the octet of
-// block jb spans that chunk and the next one, which the lane 16 above holds,
-// so a lane rotation brings it in and a per-lane byte shift (the row's offset
-// inside its first chunk, the same in every step) cuts the octet out.  Every
-// load is an aligned dwordx4.  KAL = 2 / 1 (keep above 96, where the extra
-// chunk costs too many registers): the dwordx4 at the octet's own 4-byte
-// aligned offset (even keep), or at the dword boundary below it plus the dword
-// after it with a byte shift of 0 or 2 (odd keep).  Channels past keep are
-// masked in every case but KAL = 8.
+// K_thin octets (8 channels, 16 bytes of one head row).  KAL = 8 (keep a
+// multiple of 8): head rows are 16-byte aligned and an octet is one aligned
+// dwordx4.  KAL = 0 (any other keep): each lane loads the 16-byte aligned
+// chunks 4*jb + q4 of its token row (lanes q4 = 0 one more, chunk 4*KB); the
+// octet of block jb spans that chunk and the next one, which the lane 16
+// above holds, so a lane rotation brings it in and a per-lane byte shift (the
+// row's offset inside its first chunk, the same in every step) cuts the octet
+// out, and the last block's channels past keep are masked.  Every K_thin load
+// is an aligned dwordx4.
 template <int KB, int KAL>
 struct Frag {
     uint4 k[2][KAL == 0 ? KB + 1 : KB];  // token half x 32-channel block (KAL 0: x chunk)
-    uint32_t ky[2][KAL == 1 ? KB : 1];   // KAL 1: the dword after each dwordx4
     uint4 v[8];                          // V rows of this lane's 8 tokens (16 bytes each)
 };
 
 // Lane-constant parts of the loads of one 32-token step (byte offsets from
-// the step's K_thin / V descriptor bases).
+// the step's K_thin / V descriptor bases).  Blocks before the last lie
+// inside every kept row (keep > 32 * (KB - 1)), so their chunks are a fixed
+// distance above the first; only the last block's chunk and the extra one
+// are checked per lane.  V rows of the lane's tokens differ by wave-uniform
+// offsets, passed separately.
 template <int KB>
 struct LaneOffsets {
-    uint32_t k[2][KB];       // dword-aligned offset of the octet's dwordx4; kOff when past keep
-    uint32_t ks[2][KB];      // byte shift of the octet inside that dwordx4 (KAL 1)
-    uint32_t kc[2][KB + 1];  // KAL 0: offset of chunk 4*jb + q4; kOff when not needed
-    uint32_t kr[2];          // KAL 0: the token row's byte offset inside its first chunk
-    uint4 kmask[KB];         // channel mask of the octet (all but KAL 8)
-    uint32_t v[8];           // V row of this lane's token i, channel octet n16
+    uint32_t k0[2];      // chunk q4 of the lane's token row (chunk 4*jb + q4 is 64*jb above)
+    uint32_t kt[2][2];   // chunks of the last block and the extra one; kOff when not needed
+    uint32_t kr[2];      // KAL 0: the token row's byte offset inside its first chunk
+    uint4 kmask;         // KAL 0: channel mask of the last block's octet
+    uint32_t v0;         // V: this lane's channel octet in token row 4*q4
 };
 
 // `delta` is the K_thin descriptor base's distance below the step's first
-// row of this head: the row's offset from a 16-byte boundary (KAL 0), from a
-// 4-byte boundary (KAL 1), else 0.
+// row of this head, which puts the base on a 16-byte boundary.  A chunk is
+// loaded if it starts before the row's last kept channel ends (it then lies
+// inside the descriptor's range, which is rounded up to 16 bytes); for
+// KAL = 8 that is exactly "the octet holds kept channels".
 template <int KB>
 __device__ __forceinline__ LaneOffsets<KB> lane_offsets(int keep, size_t kt_row, size_t v_row,
                                                         int n16, int q4, uint32_t delta) {
     LaneOffsets<KB> lo;
+    const int j0 = (KB - 1) * 32 + 8 * q4;       // the last block's octet
+    uint32_t mw[4];
 #pragma unroll
-    for (int jb = 0; jb < KB; ++jb) {
-        const int j0 = jb * 32 + 8 * q4;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint32_t off = (uint32_t)(((16 * h + n16) * kt_row + j0) * 2) + delta;
-            lo.ks[h][jb] = j0 < keep ? (off & 2u) : 0u;
-            lo.k[h][jb] = j0 < keep ? (off & ~3u) : kOff;
-        }
-        uint32_t mw[4];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const int j = j0 + 2 * w;
-            mw[w] = (j < keep ? 0x0000ffffu : 0u) | (j + 1 < keep ? 0xffff0000u : 0u);
-        }
-        lo.kmask[jb] = make_uint4(mw[0], mw[1], mw[2], mw[3]);
+    for (int w = 0; w < 4; ++w) {
+        const int j = j0 + 2 * w;
+        mw[w] = (j < keep ? 0x0000ffffu : 0u) | (j + 1 < keep ? 0xffff0000u : 0u);
     }
-    // KAL 0: a chunk is loaded if it starts before the row's last kept channel
-    // ends (it then lies inside the descriptor's range, which is rounded up to
-    // 16 bytes)
+    lo.kmask = make_uint4(mw[0], mw[1], mw[2], mw[3]);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const uint32_t row = (uint32_t)((16 * h + n16) * kt_row * 2) + delta;
         const uint32_t r = row & 15u, al = row & ~15u;
         lo.kr[h] = r;
+        lo.k0[h] = al + 16u * q4;
 #pragma unroll
-        for (int jb = 0; jb <= KB; ++jb) {
+        for (int e = 0; e < 2; ++e) {
+            const int jb = KB - 1 + e;
             const uint32_t k = 4u * jb + q4;
             const bool need = 16u * k < r + 2u * (uint32_t)keep && (jb < KB || q4 == 0);
-            lo.kc[h][jb] = need ? al + 16u * k : kOff;
+            lo.kt[h][e] = need ? al + 16u * k : kOff;
         }
     }
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        lo.v[i] = (uint32_t)(((4 * q4 + (i & 3) + 16 * (i >> 2)) * v_row + 8 * n16) * 2);
+    lo.v0 = (uint32_t)((4 * q4 * v_row + 8 * n16) * 2);
     return lo;
 }
 
 // Issue the loads of one 32-token step: rk / rv cover this kv head's rows of
-// the step's valid tokens only, so every other read returns zero.
+// the step's valid tokens only, so every other read returns zero.  vs[i] is
+// the wave-uniform offset of token row (i & 3) + 16 * (i >> 2) above row 0.
 template <int KB, int KAL>
 __device__ __forceinline__ void load_step(Frag<KB, KAL>& f, __amdgpu_buffer_rsrc_t rk,
-                                          __amdgpu_buffer_rsrc_t rv, const LaneOffsets<KB>& lo) {
-    if constexpr (KAL == 0) {
+                                          __amdgpu_buffer_rsrc_t rv, const LaneOffsets<KB>& lo,
+                                          const uint32_t (&vs)[8]) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-            for (int jb = 0; jb <= KB; ++jb) f.k[h][jb] = ldb_stream(rk, lo.kc[h][jb]);
-    } else {
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int jb = 0; jb < KB; ++jb) {
-                f.k[h][jb] = ldb_stream(rk, lo.k[h][jb]);
-                if constexpr (KAL == 1)
-                    f.ky[h][jb] = __builtin_amdgcn_raw_buffer_load_b32(
-                            rk, (int)(lo.k[h][jb] + 16u), 0, kNonTemporal);
-            }
+        for (int jb = 0; jb < KB - 1; ++jb) f.k[h][jb] = ldb_stream(rk, lo.k0[h] + 64u * jb);
+        f.k[h][KB - 1] = ldb_stream(rk, lo.kt[h][0]);
+        if constexpr (KAL == 0) f.k[h][KB] = ldb_stream(rk, lo.kt[h][1]);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) f.v[i] = ldb_stream(rv, lo.v[i]);
-}
-
-// The logits' A operand for one octet, from the loaded words.
-template <int KB, int KAL>
-__device__ __forceinline__ uint4 k_operand(const Frag<KB, KAL>& f, const LaneOffsets<KB>& lo,
-                                           int h, int jb) {
-    const uint4 x = f.k[h][jb];
-    if constexpr (KAL == 8) {
-        return x;
-    } else if constexpr (KAL == 2) {
-        const uint4 mk = lo.kmask[jb];
-        return make_uint4(x.x & mk.x, x.y & mk.y, x.z & mk.z, x.w & mk.w);
-    } else {
-        const uint4 mk = lo.kmask[jb];
-        const uint32_t sh = lo.ks[h][jb];
-        return make_uint4(__builtin_amdgcn_alignbyte(x.y, x.x, sh) & mk.x,
-                          __builtin_amdgcn_alignbyte(x.z, x.y, sh) & mk.y,
-                          __builtin_amdgcn_alignbyte(x.w, x.z, sh) & mk.z,
-                          __builtin_amdgcn_alignbyte(f.ky[h][jb], x.w, sh) & mk.w);
+    for (int i = 0; i < 8; ++i) {
+        const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)lo.v0, (int)vs[i],
+                                                                kNonTemporal);
+        f.v[i] = make_uint4(w.x, w.y, w.z, w.w);
     }
 }
 
@@ -255,8 +221,9 @@ __device__ __forceinline__ void compute_step(const Frag<KB, KAL>& f, const LaneO
                         pick(wrap, y[jb + 1].x, y[jb].x), pick(wrap, y[jb + 1].y, y[jb].y),
                         pick(wrap, y[jb + 1].z, y[jb].z), pick(wrap, y[jb + 1].w, y[jb].w));
                 const uint4 o = window16(f.k[h][jb], nx, lo.kr[h]);
-                const uint4 mk = lo.kmask[jb];
-                const uint4 a = make_uint4(o.x & mk.x, o.y & mk.y, o.z & mk.z, o.w & mk.w);
+                const uint4 a = jb < KB - 1 ? o
+                                            : make_uint4(o.x & lo.kmask.x, o.y & lo.kmask.y,
+                                                         o.z & lo.kmask.z, o.w & lo.kmask.w);
                 if (h == 0)
                     c0 = mfma(a, qB[jb], c0);
                 else
@@ -266,8 +233,8 @@ __device__ __forceinline__ void compute_step(const Frag<KB, KAL>& f, const LaneO
     } else {
 #pragma unroll
         for (int jb = 0; jb < KB; ++jb) {
-            c0 = mfma(k_operand<KB, KAL>(f, lo, 0, jb), qB[jb], c0);
-            c1 = mfma(k_operand<KB, KAL>(f, lo, 1, jb), qB[jb], c1);
+            c0 = mfma(f.k[0][jb], qB[jb], c0);
+            c1 = mfma(f.k[1][jb], qB[jb], c1);
         }
     }
     // c0[r]: token 4*q4 + r of the step, c1[r]: token 16 + 4*q4 + r (nt of
@@ -415,26 +382,27 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode_mfma(
     // this wave's first rows of kv head kv; the valid bytes of a step starting
     // at token ts end at the last valid token's row.  Steps advance by 32 rows
     // of 2*Hkv*keep bytes, a multiple of 64, so the row's offset from a 16-byte
-    // (KAL 0) or 4-byte (KAL 1) boundary is the same in every step: the
-    // descriptor base starts `delta` bytes below the row, on that boundary
-    // (k_thin itself is 16-byte aligned, so the bytes read below the row and
-    // past the range's end stay within the 16-byte blocks of valid rows).
+    // boundary is the same in every step: the descriptor base starts `delta`
+    // bytes below the row, on that boundary (k_thin itself is 16-byte
+    // aligned, so the bytes read below the row and past the range's end stay
+    // within the 16-byte blocks of valid rows; for KAL = 8 delta is 0).
     const uint16_t* kw = k_thin + ((size_t)b * s_cap + ws) * kt_row + (size_t)kv * keep;
     const uint16_t* vw = v_cache + ((size_t)b * s_cap + ws) * v_row + (size_t)kv * kD;
-    const uint32_t delta = KAL == 0 ? (uint32_t)(reinterpret_cast<uintptr_t>(kw) & 15u)
-                           : KAL == 1 ? (uint32_t)(reinterpret_cast<uintptr_t>(kw) & 3u) : 0u;
+    const uint32_t delta = (uint32_t)(reinterpret_cast<uintptr_t>(kw) & 15u);
     const LaneOffsets<KB> lo = lane_offsets<KB>(keep, kt_row, v_row, n16, q4, delta);
+    uint32_t vs[8];                              // V rows of tokens (i & 3) + 16 * (i >> 2)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vs[i] = (uint32_t)(((i & 3) + 16 * (i >> 2)) * v_row * 2);
     // descriptors of the step starting at token ts: empty once ts >= we (a
     // wave past the length issues only empty loads, which read zeros without
     // touching memory)
     auto rsrc_k = [&](int ts) {
         const int nt = min(32, we - ts);
         // a dword reads as zero unless it ends inside the range, so the range
-        // is rounded up to whole dwords, or whole 16-byte chunks for KAL 0
-        // (the extra bytes share the last valid dword or chunk and are masked)
-        const uint32_t rnd = KAL == 0 ? 15u : 3u;
+        // is rounded up to whole 16-byte chunks (the extra bytes share the
+        // last valid chunk and are masked)
         const uint32_t bytes =
-                nt > 0 ? ((uint32_t)(((nt - 1) * kt_row + keep) * 2) + delta + rnd) & ~rnd : 0u;
+                nt > 0 ? ((uint32_t)(((nt - 1) * kt_row + keep) * 2) + delta + 15u) & ~15u : 0u;
         return make_rsrc(reinterpret_cast<const char*>(kw + (size_t)(ts - ws) * kt_row) - delta,
                          bytes);
     };
@@ -449,8 +417,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode_mfma(
     // has an empty descriptor), so the wait before each compute covers only
     // that buffer's own loads.
     Frag<KB, KAL> fa, fb;
-    load_step<KB, KAL>(fa, rsrc_k(ws), rsrc_v(ws), lo);
-    load_step<KB, KAL>(fb, rsrc_k(ws + 32), rsrc_v(ws + 32), lo);
+    load_step<KB, KAL>(fa, rsrc_k(ws), rsrc_v(ws), lo, vs);
+    load_step<KB, KAL>(fb, rsrc_k(ws + 32), rsrc_v(ws + 32), lo, vs);
 
 #pragma unroll
     for (int r = 0; r < kGather; ++r) {
@@ -471,10 +439,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_decode_mfma(
 
     for (int ts = ws; ts < we; ts += 64) {
         compute_step<KB, KAL>(fa, lo, min(32, we - ts), scale, qB, q4, O, m, l);
-        load_step<KB, KAL>(fa, rsrc_k(ts + 64), rsrc_v(ts + 64), lo);
+        load_step<KB, KAL>(fa, rsrc_k(ts + 64), rsrc_v(ts + 64), lo, vs);
         if (ts + 32 < we)
             compute_step<KB, KAL>(fb, lo, min(32, we - ts - 32), scale, qB, q4, O, m, l);
-        load_step<KB, KAL>(fb, rsrc_k(ts + 96), rsrc_v(ts + 96), lo);
+        load_step<KB, KAL>(fb, rsrc_k(ts + 96), rsrc_v(ts + 96), lo, vs);
     }
 
     // ---- merge the 4 waves (a wave past len_b has m = -inf, l = 0, O = 0)
@@ -522,18 +490,8 @@ hipError_t launch_kb(int kal, dim3 grid, hipStream_t s, const uint16_t* q, const
     if (kal == 8)
         k_decode_mfma<KB, 8><<<grid, kThreads, 0, s>>>(q, kt, v, lens, idx, s_cap, Hkv, G, keep,
                                                        scale, chunk, nsplit, rec, mode, part);
-    else if (kal == 0) {
-        if constexpr (KB < 4)
-            k_decode_mfma<KB, 0><<<grid, kThreads, 0, s>>>(q, kt, v, lens, idx, s_cap, Hkv, G,
-                                                           keep, scale, chunk, nsplit, rec, mode,
-                                                           part);
-        else
-            return hipErrorInvalidValue;
-    } else if (kal == 2)
-        k_decode_mfma<KB, 2><<<grid, kThreads, 0, s>>>(q, kt, v, lens, idx, s_cap, Hkv, G, keep,
-                                                       scale, chunk, nsplit, rec, mode, part);
     else
-        k_decode_mfma<KB, 1><<<grid, kThreads, 0, s>>>(q, kt, v, lens, idx, s_cap, Hkv, G, keep,
+        k_decode_mfma<KB, 0><<<grid, kThreads, 0, s>>>(q, kt, v, lens, idx, s_cap, Hkv, G, keep,
                                                        scale, chunk, nsplit, rec, mode, part);
     return hipGetLastError();
 }
@@ -565,7 +523,7 @@ hipError_t launch_decode_mfma(const think_dims& d, const DecodeGeom& g, const vo
                               const int32_t* kept_idx, int keep, float scale, float* partials,
                               hipStream_t s) {
     const int G = d.n_q_heads / d.n_kv_heads;
-    const int kal = keep % 8 == 0 ? 8 : keep <= 96 ? 0 : keep % 2 == 0 ? 2 : 1;
+    const int kal = keep % 8 == 0 ? 8 : 0;
     const int KB = (keep + 31) / 32;
     dim3 grid(g.nsplit, d.n_kv_heads, d.batch);
     auto qp = (const uint16_t*)q;
