@@ -286,7 +286,7 @@ __device__ __forceinline__ void compute_step(const Frag<KB, KAL>& f, const LaneO
 }
 
 template <int KB, int KAL>
-__global__ __launch_bounds__(kThreads, 2) void k_decode_mfma(
+__global__ __launch_bounds__(kThreads, (KAL == 8 && KB <= 2) ? 3 : 2) void k_decode_mfma(
         const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_thin,
         const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ seq_lens,
         const int32_t* __restrict__ kept_idx, int s_cap, int Hkv, int G, int keep, float scale,
@@ -506,11 +506,16 @@ bool mfma_decode_supported(const think_dims& d, int keep) {
 // Tokens per workgroup: a multiple of 128 (one 32-token step per wave), sized
 // for about 512 workgroups (two per CU) and at most 256 chunks per sequence,
 // and at least 512 (four steps per wave) so the prologue and the merge stay
-// small next to the stream when there are many kv heads and few tokens.
+// small next to the stream when there are many kv heads and few tokens.  A
+// batch of 2..64 sequences with 16-byte aligned thin rows of at most 64
+// channels (an instance small enough for three workgroups per CU) is sized
+// for about 768: measured faster there (8 x 16K, keep 64: 75.7 -> 71.7 us),
+// while one sequence streams best at two per CU (128K: 69 -> 71.5 us at 768).
 int mfma_decode_chunk(const think_dims& d, int keep) {
-    (void)keep;
+    const bool three = d.batch >= 2 && d.batch <= 64 && keep % 8 == 0 && keep <= 64;
+    const int64_t wgs = three ? 768 : 512;
     const int64_t work = (int64_t)d.seq_capacity * d.n_kv_heads * d.batch;
-    int64_t chunk = (work + 511) / 512;
+    int64_t chunk = (work + wgs - 1) / wgs;
     const int64_t min_chunk = ((int64_t)d.seq_capacity + 255) / 256;
     if (chunk < min_chunk) chunk = min_chunk;
     chunk = (chunk + 127) / 128 * 128;
