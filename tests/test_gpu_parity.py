@@ -171,6 +171,10 @@ EDGE = [
          lowrank=8),
     dict(seed=18, lens=[(i * 53) % 600 + 1 for i in range(65)], batch=65, n_q_heads=4,
          n_kv_heads=1, head_dim=128, seq_capacity=600, keep=64, dtype="bf16", lowrank=8),
+    # a batch with aligned thin rows of one 32-channel block (three workgroups
+    # per CU)
+    dict(seed=20, lens=[4000, 2047, 1], batch=3, n_q_heads=12, n_kv_heads=2, head_dim=128,
+         seq_capacity=4000, keep=24, dtype="bf16", lowrank=8),
     # one long sequence among 63 of 1-5 tokens: it takes almost every slot
     dict(seed=19, lens=[6000] + [1 + i % 5 for i in range(63)], batch=64, n_q_heads=4,
          n_kv_heads=1, head_dim=128, seq_capacity=6000, keep=77, dtype="bf16", lowrank=8),
