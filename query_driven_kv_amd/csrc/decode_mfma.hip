@@ -6,16 +6,19 @@
 //   l_t = scale * sum_j q[b,h,idx_j] * K_thin[b,t,kv,j],  out = softmax(l) . V[b,:,kv,:]
 //
 // Work decomposition.  Workgroup = (token chunk, kv head, b), 4 waves; each
-// wave walks its quarter of the chunk 32 tokens at a time.  The chunk size
-// follows the sequence's own length (all nsplit chunks of a sequence carry
-// tokens), so ragged batches and partly filled caches stay balanced.  The
-// G <= 16 query heads of the group share every K_thin / V byte the wave
-// loads.
+// wave walks its quarter of the chunk 32 tokens at a time.  Chunk sizes follow
+// the lengths on the device: one sequence (or more than 64) spreads its tokens
+// over its nsplit chunks; a batch of 2..64 deals its B * nsplit chunk slots in
+// proportion to length (balanced_slots).  Ragged batches and partly filled
+// caches stay balanced.  The G <= 16 query heads of the group share every
+// K_thin / V byte the wave loads.
 //
 // Both products run on v_mfma_f32_16x16x32_bf16 (16x16 output, K = 32):
 //   logits  C[t][g] = sum_j K_thin[t][j] * qS[j][g]
-//           A = K_thin rows: lane (l%16 = token, l/16 = channel octet) loads 16
-//               contiguous bytes straight from HBM;  B = gathered query,
+//           A = K_thin rows: lane (l%16 = token, l/16 = channel octet) takes 16
+//               contiguous bytes of its row (one aligned load, or assembled
+//               from aligned chunks when keep is not a multiple of 8);
+//               B = gathered query,
 //               loaded once per wave (zero for g >= G or j >= keep).
 //           C lands as lane (l%16 = g, l/16 = token quad, reg = token).
 //   values  O[g][d] = sum_t P[g][t] * V[t][d]
