@@ -309,11 +309,15 @@ def prefill_time(wl, torch, qdk, chunk=8192, reps=3):
 
 
 def decode_source_hash():
-    import hashlib
+    """Hash of the decode kernels' code: comments and whitespace are dropped,
+    so only a change to the code itself retires the counter summary."""
+    import hashlib, re
     h = hashlib.sha256()
     for f in ("decode_mfma.hip", "decode.hip", "think_common.h"):
-        with open(os.path.join(ROOT, "query_driven_kv_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "query_driven_kv_amd", "csrc", f)) as fh:
+            code = re.sub(r"/\*.*?\*/", " ", fh.read(), flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 
