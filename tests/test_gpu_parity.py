@@ -302,3 +302,35 @@ def test_split_phase_decode_is_bitwise_the_single_call():
         torch.cuda.synchronize()
         assert torch.equal(one.view(torch.int16) if one.dtype == torch.bfloat16 else one.view(torch.int32),
                            two.view(torch.int16) if two.dtype == torch.bfloat16 else two.view(torch.int32))
+
+
+def test_random_decode_shapes_match_the_oracle():
+    """Seeded random decode shapes on the bf16 matrix-core path: batch 1-70
+    (one sequence, length-dealt slots, per-sequence chunks), every keep from
+    1 to 128 over the draws, groups of 1-16 query heads, ragged lengths.
+    Each output row within the bf16 bound of the oracle."""
+    qdk = _qdk()
+    rng = np.random.default_rng(2024)
+    bf = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16)
+    h = lambda t: t.view(torch.int16).numpy().view(np.uint16)
+    keeps = list(rng.permutation(np.arange(1, 129)))
+    for case in range(64):
+        B = int(rng.choice([1, 1, 2, 3, 5, 8, 13, 64, 70]))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 2, 4, 7, 16]))
+        S = int(rng.integers(1, 2600)) if B <= 8 else int(rng.integers(1, 300))
+        keep = int(keeps[case % len(keeps)]) if case < 56 else int(rng.choice([64, 96, 128, 8]))
+        lens = rng.integers(1, S + 1, B).astype(np.int32)
+        print(f"[case {case}] B={B} Hkv={Hkv} G={G} S={S} keep={keep}", flush=True)
+        q = bf(rng.standard_normal((B, Hkv * G, 128)))
+        thin = bf(rng.standard_normal((B, S, Hkv, keep)))
+        v = bf(rng.standard_normal((B, S, Hkv, 128)))
+        idx = np.sort(np.stack([np.stack([rng.choice(128, keep, replace=False)
+                                          for _ in range(Hkv)]) for _ in range(B)]),
+                      axis=-1).astype(np.int32)
+        out = qdk.think_decode_attn(q.cuda(), thin.cuda(), v.cuda(), to_dev(lens), to_dev(idx),
+                                    0.09)
+        torch.cuda.synchronize()
+        ref = oracle.decode(h(q), h(thin), h(v), lens, idx, np.float32(0.09))
+        err = row_rel_err(out, ref).max()
+        assert err <= 2e-2, (case, B, Hkv, G, S, keep, err)
