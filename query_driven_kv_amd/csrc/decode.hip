@@ -17,6 +17,8 @@
 // This file holds the general kernel (any dtype, any keep, G <= 16) and the
 // combine kernel.  The bf16 matrix-core kernel for the bandwidth-critical
 // shapes is in decode_mfma.hip and writes the same partial records.
+#include <type_traits>
+
 #include "think_common.h"
 
 namespace thinkkv {
@@ -35,6 +37,14 @@ constexpr int kThreads = 256;
 constexpr int kChunk = 256;    // tokens per workgroup (general kernel)
 constexpr int kMaxG = 16;
 
+// Logits and running maxima of fp32 inputs are kept in fp64: with fp32 inputs
+// of large magnitude (a logit of a few hundred has an fp32 ulp of 3e-5) an
+// fp32 logit alone would spend the fp32 accuracy bound on its rounding.  The
+// record's maximum is stored as its fp32 rounding plus the fp32 residual (in
+// the record's third word).  bf16 inputs keep fp32 throughout.
+template <int DT>
+using LogitT = typename std::conditional<DT == THINK_F32, double, float>::type;
+
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_decode_partial(
         const typename Elem<DT>::T* __restrict__ q, const typename Elem<DT>::T* __restrict__ k_thin,
@@ -50,9 +60,11 @@ __global__ __launch_bounds__(kThreads) void k_decode_partial(
     const int Hq = Hkv * G;
     const int tid = threadIdx.x;
 
+    using LT = LogitT<DT>;
     __shared__ float qs[kMaxG * 256];            // gathered query, [g][j]
-    __shared__ float p[kMaxG * kChunk];          // logits, then probabilities, [g][t]
-    __shared__ float mrow[kMaxG], lrow[kMaxG];
+    __shared__ LT p[kMaxG * kChunk];             // logits, then probabilities, [g][t]
+    __shared__ LT mrow[kMaxG];
+    __shared__ float lrow[kMaxG];
 
     for (int i = tid; i < G * keep; i += kThreads) {
         const int g = i / keep, j = i - g * keep;
@@ -64,28 +76,28 @@ __global__ __launch_bounds__(kThreads) void k_decode_partial(
 
     if (tid < nt) {
         const size_t kr = (((size_t)b * s_cap + t0 + tid) * Hkv + kv) * keep;
-        float acc[kMaxG];
+        LT acc[kMaxG];
 #pragma unroll
-        for (int g = 0; g < kMaxG; ++g) acc[g] = 0.0f;
+        for (int g = 0; g < kMaxG; ++g) acc[g] = 0;
         for (int j = 0; j < keep; ++j) {
-            const float x = E::load(k_thin, kr + j);
+            const LT x = E::load(k_thin, kr + j);
 #pragma unroll
             for (int g = 0; g < kMaxG; ++g)
-                if (g < G) acc[g] = fmaf(qs[g * keep + j], x, acc[g]);
+                if (g < G) acc[g] = fma((LT)qs[g * keep + j], x, acc[g]);
         }
 #pragma unroll
         for (int g = 0; g < kMaxG; ++g)
-            if (g < G) p[g * kChunk + tid] = acc[g] * scale;
+            if (g < G) p[g * kChunk + tid] = acc[g] * (LT)scale;
     }
     __syncthreads();
 
     if (tid < G) {
-        float* pr = p + tid * kChunk;
-        float m = pr[0];
-        for (int t = 1; t < nt; ++t) m = fmaxf(m, pr[t]);
+        LT* pr = p + tid * kChunk;
+        LT m = pr[0];
+        for (int t = 1; t < nt; ++t) m = pr[t] > m ? pr[t] : m;
         float l = 0.0f;
         for (int t = 0; t < nt; ++t) {
-            const float e = expf(pr[t] - m);
+            const float e = expf((float)(pr[t] - m));
             pr[t] = e;
             l += e;
         }
@@ -102,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_partial(
             const float v = E::load(v_cache, (((size_t)b * s_cap + t0 + t) * Hkv + kv) * D + d);
 #pragma unroll
             for (int g = 0; g < kMaxG; ++g)
-                if (g < G) o[g] = fmaf(p[g * kChunk + t], v, o[g]);
+                if (g < G) o[g] = fmaf((float)p[g * kChunk + t], v, o[g]);
         }
 #pragma unroll
         for (int g = 0; g < kMaxG; ++g)
@@ -111,8 +123,10 @@ __global__ __launch_bounds__(kThreads) void k_decode_partial(
     }
     if (tid < G) {
         float* r = partials + (((size_t)b * Hq + kv * G + tid) * nsplit + split) * rec;
-        r[0] = mrow[tid];
+        const LT m = mrow[tid];
+        r[0] = (float)m;
         r[1] = lrow[tid];
+        r[2] = (float)(m - (LT)(float)m);        // zero for bf16
     }
 }
 
@@ -132,7 +146,8 @@ __global__ __launch_bounds__(1024) void k_decode_combine(
         int chunk, int mode, int nsplit, int rec, int D, int sg_count,
         typename Elem<DT>::T* __restrict__ out) {
     using E = Elem<DT>;
-    constexpr float kNone = -3.402823466e38f;   // finite stand-in for an empty maximum
+    using MT = LogitT<DT>;
+    constexpr MT kNone = -3.402823466e38f;      // finite stand-in for an empty maximum
     const int h = blockIdx.x, b = blockIdx.y, Hq = gridDim.x, nb = gridDim.y;
     const int tid = threadIdx.x;
     const int D4 = D >> 2;
@@ -155,15 +170,25 @@ __global__ __launch_bounds__(1024) void k_decode_combine(
     }
     const int lo = (int)((unsigned)(sg * nrange) / (unsigned)sg_count);
     const int hi = (int)((unsigned)((sg + 1) * nrange) / (unsigned)sg_count);
-    float M = kNone, L = 0.0f;
+    MT M = kNone;
+    float L = 0.0f;
     float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s0 = lo; s0 < hi; s0 += 8) {
-        float2 ml[8];
+        MT mk[8];
+        float lk[8];
         float4 ov[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const float* r = base + (size_t)min(s0 + k, nrange - 1) * rec;
-            ml[k] = *reinterpret_cast<const float2*>(r);
+            if constexpr (DT == THINK_F32) {
+                const float4 h4 = *reinterpret_cast<const float4*>(r);
+                mk[k] = (MT)h4.x + (MT)h4.z;     // maximum plus its residual
+                lk[k] = h4.y;
+            } else {
+                const float2 h2 = *reinterpret_cast<const float2*>(r);
+                mk[k] = h2.x;
+                lk[k] = h2.y;
+            }
             ov[k] = *reinterpret_cast<const float4*>(r + 4 + 4 * d4);
         }
         // the record loads above are issued before the length is waited on
@@ -171,18 +196,19 @@ __global__ __launch_bounds__(1024) void k_decode_combine(
         const int len = len_raw < 0 ? 0 : (len_raw > s_cap ? s_cap : len_raw);
         const int cb = mode == kSeqChunk ? seq_chunk(len, chunk, nsplit) : chunk;
         const int ns = mode == kBalanced ? used : (len + cb - 1) / cb;
-        float mv[8], lv[8];
+        MT mv[8];
+        float lv[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const bool ok = s0 + k < hi && s0 + k < ns;
-            mv[k] = ok ? ml[k].x : kNone;
-            lv[k] = ok ? ml[k].y : 0.0f;
+            mv[k] = ok ? mk[k] : kNone;
+            lv[k] = ok ? lk[k] : 0.0f;
             if (!ok) ov[k] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
-        float Mn = M;
+        MT Mn = M;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) Mn = fmaxf(Mn, mv[k]);
-        const float f = expf(M - Mn);
+        for (int k = 0; k < 8; ++k) Mn = mv[k] > Mn ? mv[k] : Mn;
+        const float f = expf((float)(M - Mn));
         L *= f;
         O.x *= f;
         O.y *= f;
@@ -190,7 +216,7 @@ __global__ __launch_bounds__(1024) void k_decode_combine(
         O.w *= f;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            const float w = expf(mv[k] - Mn);
+            const float w = expf((float)(mv[k] - Mn));
             L = fmaf(w, lv[k], L);
             O.x = fmaf(w, ov[k].x, O.x);
             O.y = fmaf(w, ov[k].y, O.y);
@@ -199,7 +225,8 @@ __global__ __launch_bounds__(1024) void k_decode_combine(
         }
         M = Mn;
     }
-    __shared__ float sM[64], sL[64];
+    __shared__ MT sM[64];
+    __shared__ float sL[64];
     __shared__ float4 sO[1024];
     if (d4 == 0) {
         sM[sg] = M;
@@ -208,12 +235,12 @@ __global__ __launch_bounds__(1024) void k_decode_combine(
     sO[tid] = O;
     __syncthreads();
     if (sg == 0) {
-        float MM = sM[0];
-        for (int r = 1; r < sg_count; ++r) MM = fmaxf(MM, sM[r]);
+        MT MM = sM[0];
+        for (int r = 1; r < sg_count; ++r) MM = sM[r] > MM ? sM[r] : MM;
         float LL = 0.0f;
         float4 OO = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int r = 0; r < sg_count; ++r) {
-            const float f = sL[r] > 0.0f ? expf(sM[r] - MM) : 0.0f;
+            const float f = sL[r] > 0.0f ? expf((float)(sM[r] - MM)) : 0.0f;
             const float4 o = sO[r * D4 + d4];
             LL = fmaf(f, sL[r], LL);
             OO.x = fmaf(f, o.x, OO.x);

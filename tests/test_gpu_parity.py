@@ -334,3 +334,27 @@ def test_random_decode_shapes_match_the_oracle():
         ref = oracle.decode(h(q), h(thin), h(v), lens, idx, np.float32(0.09))
         err = row_rel_err(out, ref).max()
         assert err <= 2e-2, (case, B, Hkv, G, S, keep, err)
+
+
+def test_random_full_path_shapes_match_the_oracle():
+    """Seeded random shapes through score, selection, compaction and decode:
+    bf16 and fp32, head_dim 8-256, ragged batches of 1-66 sequences, keep from
+    1 to head_dim, windows of 1-40 queries."""
+    rng = np.random.default_rng(77)
+    for case in range(16):
+        dtype = "bf16" if case % 4 else "f32"
+        D = int(rng.choice([128, 128, 64, 256, 8, 40])) if dtype == "f32" else \
+            int(rng.choice([128, 128, 128, 64, 256]))
+        B = int(rng.choice([1, 2, 3, 7, 66]))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 2, 4, 16]))
+        while Hkv * D * (2 if dtype == "bf16" else 4) > 32768:
+            Hkv //= 2
+        S = int(rng.integers(1, 1200)) if B <= 7 else int(rng.integers(1, 120))
+        keep = int(rng.integers(1, D + 1))
+        lens = [int(x) for x in rng.integers(1, S + 1, B)]
+        lens[0] = S
+        cfg, L, q = _custom(100 + case, lens, batch=B, n_q_heads=Hkv * G, n_kv_heads=Hkv,
+                            head_dim=D, seq_capacity=S, keep=keep, dtype=dtype,
+                            obs_window=int(rng.integers(1, 41)))
+        check_all(cfg, L, keep, q, np.float32(1.0 / np.sqrt(D)), f"random{case}")
