@@ -19,10 +19,13 @@
 //                     which keeps plain loads but not non-temporal ones), the
 //                     pass reads with plain loads so that the compaction that
 //                     follows finds much of K there; larger caches are read
-//                     non-temporally.
+//                     non-temporally.  Workgroups placed after the key
+//                     workgroups sum the window queries' squares per (b, q
+//                     head, channel) in fp64 meanwhile.
 //   k_score_finalize  one workgroup per (b, kv): sums the splits in fp64 in a
-//                     fixed order, forms the score and optionally selects the
-//                     kept channels right there.
+//                     fixed order, forms the score from them and the window
+//                     sums, and optionally selects the kept channels right
+//                     there.
 // No atomics: results are bitwise reproducible.
 #include "select_row.h"
 
@@ -32,14 +35,68 @@ namespace {
 constexpr int kThreads = 512;   // partial pass: ~256 workgroups of 8 waves stream K best
 constexpr int kColGroup = 256;  // 16-byte column vectors per workgroup
 constexpr int kRun = 16;   // tokens per fp32 run before folding into fp64
+constexpr int kQVec = 32;  // window-row vectors per window-query workgroup
 
 template <int DT, bool KEEP_IN_LLC>
 __global__ __launch_bounds__(kThreads) void k_score_partial(
         const uint4* __restrict__ k_vec, const int32_t* __restrict__ seq_lens, int s_cap,
-        int nvec, int tpw, int nsplit, float* __restrict__ partials) {
+        int nvec, int tpw, int nsplit, int ncg, float* __restrict__ partials, int nb,
+        const uint4* __restrict__ q_vec, int W, int nqv, double* __restrict__ q2) {
     using E = Elem<DT>;
     constexpr int EPV = E::kPerVec;
-    const int split = blockIdx.x, cg = blockIdx.y, b = blockIdx.z;
+    // one-dimensional grid: the key workgroups (split fastest, then column
+    // group, then sequence), then the window-query workgroups
+    const uint32_t nkey = (uint32_t)nsplit * ncg * nb;
+    const uint32_t wg = blockIdx.x;
+    const int split = (int)(wg % nsplit), cg = (int)(wg / nsplit % ncg);
+    int b = (int)(wg / ((uint32_t)nsplit * ncg));
+    __shared__ double red[kThreads * 8];         // lane sums, reduced in a fixed order
+    if (wg >= nkey) {
+        // window-query sums of squares of sequence b, for every query head and
+        // channel: Q2[b][h][c] = sum over the W window rows in fp64 (a bf16 or
+        // fp32 square is exact in fp64).  Each window-query workgroup takes
+        // kQVec 16-byte vectors of the window row; its lanes split
+        // the rows into kQGroups contiguous groups, summed in row order, and
+        // the groups are added in ascending order.  They come after every key
+        // workgroup in the grid, so they are dispatched last and never delay
+        // the key stream.
+        const int nqb = (nqv + kQVec - 1) / kQVec;           // units per sequence
+        const int u = (int)(wg - nkey);
+        const int qb = u % nqb;
+        b = u / nqb;
+        constexpr int kQGroups = kThreads / kQVec;
+        const int vq = qb * kQVec + (int)threadIdx.x % kQVec;
+        const int rg = (int)threadIdx.x / kQVec;
+        const int i0 = rg * W / kQGroups, i1 = (rg + 1) * W / kQGroups;
+        const uint4* src = q_vec + (size_t)b * W * nqv + min(vq, nqv - 1);
+        double acc[EPV];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) acc[e] = 0.0;
+        for (int i = i0; i < i1; i += 8) {
+            uint4 x[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) x[k] = src[(size_t)min(i + k, W - 1) * nqv];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                float f[EPV];
+                unpack(x[k], f, E{});
+                const bool ok = i + k < i1;
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) acc[e] += ok ? (double)f[e] * (double)f[e] : 0.0;
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) red[(rg * kQVec + threadIdx.x % kQVec) * EPV + e] = acc[e];
+        __syncthreads();
+        for (int o = threadIdx.x; o < kQVec * EPV; o += kThreads) {
+            const int v = qb * kQVec + o / EPV;
+            if (v >= nqv) continue;
+            double t = 0.0;
+            for (int r = 0; r < kQGroups; ++r) t += red[r * kQVec * EPV + o];
+            q2[(size_t)b * nqv * EPV + (size_t)v * EPV + o % EPV] = t;
+        }
+        return;
+    }
     const int len = clamp_len(seq_lens, b, s_cap);
     const int t0 = split * tpw;
     if (t0 >= len) return;                       // finalize never reads this split
@@ -82,7 +139,6 @@ __global__ __launch_bounds__(kThreads) void k_score_partial(
         }
     }
 
-    __shared__ double red[kThreads * 8];
     if (active) {
 #pragma unroll
         for (int e = 0; e < EPV; ++e) red[(rsub * nvg + col) * EPV + e] = acc[e];
@@ -101,7 +157,9 @@ __global__ __launch_bounds__(kThreads) void k_score_partial(
 //  K2:  thread (channel quad cq, split group sg) sums splits sg, sg+SG, ...
 //       in ascending order, reading float4 partials eight splits at a time
 //       so the loads overlap; the SG group sums are added in ascending order.
-//  Q:   the group's window rows hold G*D contiguous query elements; thread
+//  Q:   from the cache path, the window-query sums Q2 the partial pass wrote
+//       (q2 [B][Hq][D] fp64).  From the prefill state (STATE), the group's
+//       window rows (G*D contiguous query elements) are summed here: thread
 //       (16-byte vector v, row group rg) sums the squares of its vector over
 //       a contiguous range of rows (loads issued eight rows at a time); the
 //       row groups are added in ascending order.
@@ -112,8 +170,9 @@ __global__ __launch_bounds__(kThreads) void k_score_partial(
 template <int DT, bool SELECT, bool STATE>
 __global__ __launch_bounds__(1024) void k_score_finalize(
         const void* __restrict__ part, const int32_t* __restrict__ seq_lens, int s_cap,
-        int tpw, int nsplit, const typename Elem<DT>::T* __restrict__ q_obs, int W, int Hq,
-        int Hkv, int D, float* __restrict__ scores, int keep, int32_t* __restrict__ kept_idx,
+        int tpw, int nsplit, const typename Elem<DT>::T* __restrict__ q_obs,
+        const double* __restrict__ q2, int W, int Hq, int Hkv, int D,
+        float* __restrict__ scores, int keep, int32_t* __restrict__ kept_idx,
         int32_t* __restrict__ near_tie) {
     using E = Elem<DT>;
     constexpr int EPV = E::kPerVec;
@@ -152,14 +211,21 @@ __global__ __launch_bounds__(1024) void k_score_finalize(
     if (RG > W) RG = W;
     if (RG < 1) RG = 1;
     const int qv = tid % nv, rg = tid / nv;
-    const bool qact = rg < RG;
+    const bool qact = STATE && rg < RG;
     const int i0 = qact ? rg * W / RG : 0, i1 = qact ? (rg + 1) * W / RG : 0;
     const uint4* qb = reinterpret_cast<const uint4*>(
         q_obs + ((size_t)b * W * Hq + (size_t)kv * G) * D) + qv;
     const size_t rstride = (size_t)Hq * D / EPV;     // vectors between window rows
     uint4 x[8];
+    if constexpr (STATE) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) x[k] = qb[(size_t)min(i0 + k, W - 1) * rstride];
+        for (int k = 0; k < 8; ++k) x[k] = qb[(size_t)min(i0 + k, W - 1) * rstride];
+    } else {
+        // the group's Q2 rows straight into their norms (read before any wait
+        // on the partials, so both loads overlap)
+        const double* qs = q2 + ((size_t)b * Hq + (size_t)kv * G) * D;
+        for (int pr = tid; pr < GD; pr += nth) qn[pr] = sqrt(qs[pr]);
+    }
 
     if constexpr (STATE) {
         // four channels per thread as two 16-byte double pairs per slot
@@ -231,27 +297,31 @@ __global__ __launch_bounds__(1024) void k_score_finalize(
             for (int e = 0; e < EPV; ++e) acc[e] += ok ? (double)f[e] * (double)f[e] : 0.0;
         }
     };
-    if (i0 < i1) addq(x, i0);
-    for (int i = i0 + 8; i < i1; i += 8) {
+    if constexpr (STATE) {
+        if (i0 < i1) addq(x, i0);
+        for (int i = i0 + 8; i < i1; i += 8) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) x[k] = qb[(size_t)min(i + k, W - 1) * rstride];
-        addq(x, i);
+            for (int k = 0; k < 8; ++k) x[k] = qb[(size_t)min(i + k, W - 1) * rstride];
+            addq(x, i);
+        }
     }
 
     __syncthreads();
     double K2 = 0.0;
     if (tid < D)
         for (int r = 0; r < SG; ++r) K2 += red[r * D + tid];
-    __syncthreads();                             // red is reused below
-    if (qact) {
+    if constexpr (STATE) {
+        __syncthreads();                         // red is reused below
+        if (qact) {
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) red[rg * GD + qv * EPV + e] = acc[e];
-    }
-    __syncthreads();
-    for (int pr = tid; pr < GD; pr += nth) {
-        double t = 0.0;
-        for (int r = 0; r < RG; ++r) t += red[r * GD + pr];
-        qn[pr] = sqrt(t);                        // index g*D + c
+            for (int e = 0; e < EPV; ++e) red[rg * GD + qv * EPV + e] = acc[e];
+        }
+        __syncthreads();
+        for (int pr = tid; pr < GD; pr += nth) {
+            double t = 0.0;
+            for (int r = 0; r < RG; ++r) t += red[r * GD + pr];
+            qn[pr] = sqrt(t);                    // index g*D + c
+        }
     }
     __syncthreads();
 
@@ -289,7 +359,11 @@ ScoreGeom score_geom(const think_dims& d) {
     // of that much was measured 1.6-1.9x faster than the first on this part
     const size_t k_bytes = (size_t)d.batch * d.seq_capacity * g.nvec * 16;
     g.keep_in_llc = k_bytes <= ((size_t)192 << 20);
-    g.ws_bytes = (size_t)d.batch * g.nsplit * d.n_kv_heads * d.head_dim * sizeof(float);
+    // fp32 partials [B][nsplit][Hkv*D], then (16-byte aligned) the window
+    // query sums Q2 [B][Hq][D] fp64
+    g.q2_offset = ((size_t)d.batch * g.nsplit * d.n_kv_heads * d.head_dim * sizeof(float) + 15) /
+                  16 * 16;
+    g.ws_bytes = g.q2_offset + (size_t)d.batch * d.n_q_heads * d.head_dim * sizeof(double);
     return g;
 }
 
@@ -298,7 +372,11 @@ hipError_t launch_score(const think_dims& d, const ScoreGeom& g, const void* k_c
                         void* workspace, int keep, int32_t* kept_idx, int32_t* near_tie,
                         hipStream_t s) {
     float* partials = reinterpret_cast<float*>(workspace);
-    dim3 grid1(g.nsplit, g.ncg, d.batch);
+    double* q2 = reinterpret_cast<double*>(static_cast<char*>(workspace) + g.q2_offset);
+    const int nqv = d.n_q_heads * d.head_dim * elem_bytes(d.dtype) / 16;
+    // key workgroups, then the window-query workgroups, in one dimension
+    const size_t nq_units = (size_t)d.batch * ((nqv + kQVec - 1) / kQVec);
+    dim3 grid1((unsigned)((size_t)g.nsplit * g.ncg * d.batch + nq_units));
     const int Q = d.head_dim / 4;
     int sg = 1024 / Q;
     if (sg > 64) sg = 64;
@@ -306,27 +384,24 @@ hipError_t launch_score(const think_dims& d, const ScoreGeom& g, const void* k_c
     const int threads2 = Q * sg;
 #define THINK_FINALIZE(DT, SEL, T)                                                               \
     k_score_finalize<DT, SEL, false><<<grid2, threads2, 0, s>>>(                                \
-        partials, seq_lens, d.seq_capacity, g.tpw, g.nsplit, (const T*)q_obs, W, d.n_q_heads,   \
-        d.n_kv_heads, d.head_dim, scores, keep, kept_idx, near_tie)
+        partials, seq_lens, d.seq_capacity, g.tpw, g.nsplit, (const T*)q_obs, q2, W,            \
+        d.n_q_heads, d.n_kv_heads, d.head_dim, scores, keep, kept_idx, near_tie)
+#define THINK_PARTIAL(DT, LLC)                                                                   \
+    k_score_partial<DT, LLC><<<grid1, kThreads, 0, s>>>(                                        \
+        (const uint4*)k_cache, seq_lens, d.seq_capacity, g.nvec, g.tpw, g.nsplit, g.ncg,         \
+        partials, d.batch, (const uint4*)q_obs, W, nqv, q2)
     if (d.dtype == THINK_BF16) {
-        if (g.keep_in_llc)
-            k_score_partial<THINK_BF16, true><<<grid1, kThreads, 0, s>>>(
-                (const uint4*)k_cache, seq_lens, d.seq_capacity, g.nvec, g.tpw, g.nsplit, partials);
-        else
-            k_score_partial<THINK_BF16, false><<<grid1, kThreads, 0, s>>>(
-                (const uint4*)k_cache, seq_lens, d.seq_capacity, g.nvec, g.tpw, g.nsplit, partials);
+        if (g.keep_in_llc) THINK_PARTIAL(THINK_BF16, true);
+        else THINK_PARTIAL(THINK_BF16, false);
         if (kept_idx) THINK_FINALIZE(THINK_BF16, true, uint16_t);
         else THINK_FINALIZE(THINK_BF16, false, uint16_t);
     } else {
-        if (g.keep_in_llc)
-            k_score_partial<THINK_F32, true><<<grid1, kThreads, 0, s>>>(
-                (const uint4*)k_cache, seq_lens, d.seq_capacity, g.nvec, g.tpw, g.nsplit, partials);
-        else
-            k_score_partial<THINK_F32, false><<<grid1, kThreads, 0, s>>>(
-                (const uint4*)k_cache, seq_lens, d.seq_capacity, g.nvec, g.tpw, g.nsplit, partials);
+        if (g.keep_in_llc) THINK_PARTIAL(THINK_F32, true);
+        else THINK_PARTIAL(THINK_F32, false);
         if (kept_idx) THINK_FINALIZE(THINK_F32, true, float);
         else THINK_FINALIZE(THINK_F32, false, float);
     }
+#undef THINK_PARTIAL
 #undef THINK_FINALIZE
     return hipGetLastError();
 }
@@ -341,7 +416,7 @@ hipError_t launch_score_k2(const think_dims& d, int nslots, const double* state,
     const int threads2 = Q * sg;
 #define THINK_FINALIZE_K2(DT, SEL, T)                                                            \
     k_score_finalize<DT, SEL, true><<<grid2, threads2, 0, s>>>(                                 \
-        state, nullptr, d.seq_capacity, 1, nslots, (const T*)q_obs, W, d.n_q_heads,             \
+        state, nullptr, d.seq_capacity, 1, nslots, (const T*)q_obs, nullptr, W, d.n_q_heads,    \
         d.n_kv_heads, d.head_dim, scores, keep, kept_idx, near_tie)
     if (d.dtype == THINK_BF16) {
         if (kept_idx) THINK_FINALIZE_K2(THINK_BF16, true, uint16_t);

@@ -66,7 +66,7 @@ int think_score(const think_dims* d, const void* k_cache, const int32_t* seq_len
     if (st != THINK_OK) return st;
     if (!k_cache || !seq_lens || !q_obs || !scores) return THINK_ERR_NULL;
     if (obs_window < 1) return THINK_ERR_SHAPE;
-    if (!aligned16(k_cache)) return THINK_ERR_UNSUPPORTED;
+    if (!aligned16(k_cache) || !aligned16(q_obs)) return THINK_ERR_UNSUPPORTED;
     const thinkkv::ScoreGeom g = thinkkv::score_geom(*d);
     if (!workspace || workspace_bytes < g.ws_bytes || !aligned16(workspace))
         return THINK_ERR_WORKSPACE;
@@ -84,7 +84,7 @@ int think_score_select(const think_dims* d, const void* k_cache, const int32_t* 
     if (!k_cache || !seq_lens || !q_obs || !kept_idx) return THINK_ERR_NULL;
     if (obs_window < 1) return THINK_ERR_SHAPE;
     if (keep < 1 || keep > d->head_dim) return THINK_ERR_KEEP;
-    if (!aligned16(k_cache)) return THINK_ERR_UNSUPPORTED;
+    if (!aligned16(k_cache) || !aligned16(q_obs)) return THINK_ERR_UNSUPPORTED;
     const thinkkv::ScoreGeom g = thinkkv::score_geom(*d);
     if (!workspace || workspace_bytes < g.ws_bytes || !aligned16(workspace))
         return THINK_ERR_WORKSPACE;

@@ -164,7 +164,8 @@ struct ScoreGeom {
     int tpw;           // tokens per workgroup
     int nsplit;        // token splits per sequence
     bool keep_in_llc;  // read K with plain loads (it fits the last-level cache)
-    size_t ws_bytes;   // fp32 partials [B][nsplit][Hkv*D]
+    size_t q2_offset;  // byte offset of the window-query sums in the workspace
+    size_t ws_bytes;   // fp32 partials [B][nsplit][Hkv*D], then Q2 [B][Hq][D] fp64
 };
 ScoreGeom score_geom(const think_dims& d);
 

@@ -158,6 +158,10 @@ def test_null_keep_window_workspace_and_alignment(L):
     assert lib.think_score(ctypes.byref(d), FAKE, FAKE, FAKE, 32, FAKE, None, big, None) == -6
     assert lib.think_score(ctypes.byref(d), ctypes.c_void_p(0x100002), FAKE, FAKE, 32, FAKE, FAKE,
                            big, None) == -5
+    assert lib.think_score(ctypes.byref(d), FAKE, FAKE, ctypes.c_void_p(0x100004), 32, FAKE, FAKE,
+                           big, None) == -5
+    assert lib.think_score_select(ctypes.byref(d), FAKE, FAKE, ctypes.c_void_p(0x100008), 32, 8,
+                                  None, FAKE, None, FAKE, big, None) == -5
     for keep in (0, 129):
         assert lib.think_select(ctypes.byref(d), FAKE, keep, FAKE, None, None) == -3
         assert lib.think_compact_k(ctypes.byref(d), FAKE, FAKE, FAKE, keep, FAKE, None) == -3
