@@ -63,6 +63,13 @@ static int lens_ok(int B, int S_cap, const int32_t *lens) {
     return 1;
 }
 
+/* the append alone also takes empty sequences: their first row is row 0 */
+static int lens_ok_or_empty(int B, int S_cap, const int32_t *lens) {
+    for (int b = 0; b < B; ++b)
+        if (lens[b] < 0 || lens[b] > S_cap) return 0;
+    return 1;
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();
@@ -366,7 +373,8 @@ int oracle_compact(int B, int S_cap, int Hkv, int D, int dtype, const void *k_ca
  *   K_thin[b,len_b,kv,j] = k_new[b,kv,kept_idx[b,kv,j]]
  *   V[b,len_b,kv,:]      = v_new[b,kv,:]
  *   len_b               += 1
- * A sequence already at capacity is left as it is.  Byte copies.
+ * A sequence already at capacity is left as it is; an empty one (len_b = 0)
+ * gets row 0.  Byte copies.
  * Layouts: k_new, v_new [B,Hkv,D]; K_thin [B,S_cap,Hkv,keep]; V [B,S_cap,Hkv,D].
  * ------------------------------------------------------------------------- */
 int oracle_append(int B, int S_cap, int Hkv, int D, int dtype, const void *k_new,
@@ -374,7 +382,7 @@ int oracle_append(int B, int S_cap, int Hkv, int D, int dtype, const void *k_new
                   void *k_thin, void *v_cache) {
     if (!dims_ok(B, S_cap, Hkv, Hkv, D, dtype) || keep < 1 || keep > D) return -1;
     if (!k_new || !v_new || !seq_lens || !kept_idx || !k_thin || !v_cache) return -1;
-    if (!lens_ok(B, S_cap, seq_lens)) return -1;
+    if (!lens_ok_or_empty(B, S_cap, seq_lens)) return -1;
     for (size_t i = 0; i < (size_t)B * Hkv * keep; ++i)
         if (kept_idx[i] < 0 || kept_idx[i] >= D) return -1;
     const size_t es = elem_size(dtype);

@@ -481,6 +481,29 @@ def test_decode_after_append_attends_to_the_new_token():
     np.testing.assert_array_equal(o[0, 1], v_new[0, 0].astype(np.float64))
 
 
+def test_append_to_an_empty_sequence_starts_it_at_row_0():
+    """An empty sequence's first appended token lands in row 0 (thin row = the
+    new key at the kept channels, as compacting a one-token cache gives), its
+    length becomes 1, and decoding over that one token returns the new value
+    row exactly (a softmax over one logit is 1)."""
+    cfg, L, idx, k_new, v_new = _append_case(24, "f32", B=2, lens=(5, 9))
+    thin = oracle.compact(L["k_cache"], L["seq_lens"], idx)
+    lens0 = np.array([0, 9], np.int32)
+    kt, vc, lens2 = oracle.append(k_new, v_new, lens0, idx, thin, L["v_cache"])
+    assert lens2.tolist() == [1, 10]
+    one_k = L["k_cache"].copy()
+    one_k[0, 0] = k_new[0]
+    ref = oracle.compact(one_k, np.array([1, 1], np.int32), idx)
+    np.testing.assert_array_equal(kt[0, 0], ref[0, 0])
+    np.testing.assert_array_equal(kt[0, 1:], thin[0, 1:])
+    np.testing.assert_array_equal(vc[0, 0], v_new[0])
+    q = kvsynth.decode_q(cfg, 24, 0)
+    o = oracle.decode(q, kt, vc, lens2, idx, 0.7)
+    G = q.shape[1] // idx.shape[1]
+    for h in range(q.shape[1]):
+        np.testing.assert_array_equal(o[0, h], v_new[0, h // G].astype(np.float64))
+
+
 # --------------------------------------------------------------------------- prefill-fused scoring
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_prefill_write_places_rows_and_gathers_squares(dtype):
