@@ -258,6 +258,64 @@ def append_time(cfg, torch, qdk, dev, calls=512):
     return e0.elapsed_time(e1) * 1e3 / (calls - 1), B * Hkv * (2 * D + keep + D) * e
 
 
+def append_decode_time(wl, torch, qdk, calls=64):
+    """Decode with the generated token's append, on layer 0 copied into caches
+    with `calls` free rows past the workload's capacity: `calls` steps of
+    think_append_kv + think_decode_attn, then the same steps again (lengths
+    reset) through the fused think_append_decode_attn.  Returns microseconds
+    per step for (separate, fused); both runs must leave the same caches."""
+    from query_driven_kv_amd import _lib
+    P = ctypes.c_void_p
+    cfg, e = wl.cfg, wl.layers[0]
+    B, S, Hq, Hkv, D, keep = (cfg.batch, cfg.seq_capacity, cfg.n_q_heads, cfg.n_kv_heads,
+                              cfg.head_dim, cfg.keep)
+    dev, tdt = e["v"].device, e["v"].dtype
+    S2 = S + calls
+    thin = torch.empty(B, S2, Hkv, keep, dtype=tdt, device=dev)
+    v = torch.empty(B, S2, Hkv, D, dtype=tdt, device=dev)
+    thin[:, :S].copy_(e["thin"])
+    v[:, :S].copy_(e["v"])
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    kn = torch.randn(calls, B, Hkv, D, generator=gen).to(tdt).to(dev)
+    vn = torch.randn(calls, B, Hkv, D, generator=gen).to(tdt).to(dev)
+    q = torch.randn(calls, B, Hq, D, generator=gen).to(tdt).to(dev)
+    lens = e["lens"].clone()
+    dims = qdk.make_dims(B, Hq, Hkv, D, S2, qdk.THINK_BF16 if cfg.dtype == "bf16" else qdk.THINK_F32)
+    ws = torch.zeros(qdk.think_decode_workspace_bytes(dims, keep), dtype=torch.uint8, device=dev)
+    out = torch.empty(B, Hq, D, dtype=tdt, device=dev)
+    sp = P(torch.cuda.current_stream().cuda_stream)
+    lib, d = _lib.lib, ctypes.byref(dims)
+    ptr = lambda t: P(t.data_ptr())
+    rows = []
+    times = []
+    for fused in (False, True):
+        lens.copy_(e["lens"])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(calls):
+            if fused:
+                _lib.check("think_append_decode_attn", lib.think_append_decode_attn(
+                    d, ptr(q[i]), ptr(kn[i]), ptr(vn[i]), ptr(thin), ptr(v), ptr(lens),
+                    ptr(e["idx"]), keep, wl.scale, ptr(out), ptr(ws), ws.numel(), sp))
+            else:
+                _lib.check("think_append_kv", lib.think_append_kv(
+                    d, ptr(kn[i]), ptr(vn[i]), ptr(lens), ptr(e["idx"]), keep, ptr(thin), ptr(v),
+                    sp))
+                _lib.check("think_decode_attn", lib.think_decode_attn(
+                    d, ptr(q[i]), ptr(thin), ptr(v), ptr(lens), ptr(e["idx"]), keep, wl.scale,
+                    ptr(out), ptr(ws), ws.numel(), sp))
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3 / calls)
+        rows.append((thin[:, S - 1:].clone(), v[:, S - 1:].clone(), lens.clone()))
+    assert torch.equal(rows[0][2], e["lens"] + calls), "append did not advance every sequence"
+    for a, b in zip(rows[0], rows[1]):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)) if a.dtype != torch.int32 \
+            else torch.equal(a, b), "fused and separate appends left different caches"
+    return times[0], times[1]
+
+
 def prefill_time(wl, torch, qdk, chunk=8192, reps=3):
     """Prefill-fused scoring on layer 0 of a batch-1 workload: the prompt's K/V
     rows (the resident caches serve as the rows a prefill would produce; with
@@ -459,6 +517,8 @@ def main():
     achieved = bm["dec_call"] / (part_us * 1e-6) / 1e9 if n_part else None
     app_us, app_bytes = append_time(cfg, torch, qdk, dev)
     log(f"decode-time append: {app_us:.2f} us per call")
+    sep_us, fus_us = append_decode_time(wl, torch, qdk)
+    log(f"append+decode on layer 0: separate {sep_us:.2f} us, fused {fus_us:.2f} us per step")
     pre = None
     if cfg.batch == 1:
         pw_us, ps_us, pc_us = prefill_time(wl, torch, qdk)
@@ -515,6 +575,11 @@ def main():
             "append": {"us_per_call": round(app_us, 2), "bytes_per_call": app_bytes,
                        "note": "think_append_kv, timed apart from the step (the workload's "
                                "caches are full)"},
+            "append_decode": {"separate_us_per_step": round(sep_us, 2),
+                              "fused_us_per_step": round(fus_us, 2),
+                              "note": "layer 0 in caches with 64 free rows: 64 steps of "
+                                      "think_append_kv + think_decode_attn, then of "
+                                      "think_append_decode_attn from the same lengths"},
         },
         "roofline": {"kernel": "k_decode_mfma (think_decode_attn chunk pass)",
                      "bound": "hbm", "achieved": round(achieved, 1) if achieved else None,

@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define THINK_ABI_VERSION 3
+#define THINK_ABI_VERSION 4
 
 #ifndef THINK_API
 #define THINK_API __attribute__((visibility("default")))
@@ -207,6 +207,24 @@ THINK_API int think_decode_attn_combine(const think_dims *d, const int32_t *seq_
 THINK_API int think_append_kv(const think_dims *d, const void *k_new, const void *v_new,
                               int32_t *seq_lens, const int32_t *kept_idx, int32_t keep,
                               void *k_thin, void *v_cache, void *stream);
+
+/*
+ * think_append_kv followed by think_decode_attn, in two launches instead of
+ * three (the append is folded into the decode's merge).  The decode attends
+ * over the cached tokens and, below capacity, the new token (key k_new pruned
+ * to the kept channels, value v_new) as well; the new token's rows are then
+ * written and seq_lens advanced exactly as think_append_kv does.  A sequence
+ * at capacity gets no append and attends over its cached tokens only.
+ * Arguments as for the two calls; workspace >= think_decode_workspace_bytes
+ * (d, keep).  The output is within the decode's precision bound of the two
+ * calls' (the new token's logit is summed in a different order); the cache
+ * rows and lengths are bitwise those of think_append_kv.
+ */
+THINK_API int think_append_decode_attn(const think_dims *d, const void *q, const void *k_new,
+                                       const void *v_new, void *k_thin, void *v_cache,
+                                       int32_t *seq_lens, const int32_t *kept_idx, int32_t keep,
+                                       float softmax_scale, void *out, void *workspace,
+                                       size_t workspace_bytes, void *stream);
 
 /*
  * Prefill-fused scoring, the step before stage (a).  Stage (a) reads the keys

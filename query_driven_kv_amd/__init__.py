@@ -20,7 +20,7 @@ from ._lib import THINK_BF16, THINK_F32, ThinkError, think_dims
 __all__ = ["think_score", "think_score_select", "think_select", "think_compact_k",
            "think_decode_attn",
            "think_decode_attn_partial", "think_decode_attn_combine", "think_append_kv",
-           "think_k2_state_bytes", "think_prefill_write_kv", "think_score_select_k2",
+           "think_append_decode_attn", "think_k2_state_bytes", "think_prefill_write_kv", "think_score_select_k2",
            "think_keep_from_ratio", "think_score_workspace_bytes", "think_decode_workspace_bytes",
            "think_abi_version", "make_dims", "ThinkError", "think_dims", "LIB_PATH"]
 
@@ -244,6 +244,34 @@ def think_append_kv(k_new, v_new, seq_lens, kept_idx, k_thin, v_cache, *, stream
         ctypes.byref(dims), _p(k_new), _p(v_new), _p(seq_lens), _p(kept_idx), int(keep),
         _p(k_thin), _p(v_cache), _stream(stream)))
     return seq_lens
+
+
+def think_append_decode_attn(q, k_new, v_new, k_thin, v_cache, seq_lens, kept_idx,
+                             softmax_scale, *, out=None, workspace=None, stream=None):
+    """think_append_kv then think_decode_attn in two launches: the decode
+    attends over the cached tokens plus the new one (below capacity), whose
+    rows are then written and seq_lens advanced in place.  Returns out."""
+    _dev(q, k_new, v_new, k_thin, v_cache, seq_lens, kept_idx, out, workspace)
+    _i32(seq_lens, "seq_lens")
+    _i32(kept_idx, "kept_idx")
+    B, Hq, D = q.shape
+    _, S, Hkv, keep = k_thin.shape
+    if (tuple(v_cache.shape) != (B, S, Hkv, D) or tuple(kept_idx.shape) != (B, Hkv, keep)
+            or tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D)
+            or len({q.dtype, k_new.dtype, v_new.dtype, k_thin.dtype, v_cache.dtype}) != 1):
+        raise ValueError("shape or dtype mismatch between q, k_new, v_new, k_thin, v_cache, "
+                         "kept_idx")
+    dims = make_dims(B, Hq, Hkv, D, S, _dtype_code(q))
+    if out is None:
+        out = torch.empty(B, Hq, D, dtype=q.dtype, device=q.device)
+    need = think_decode_workspace_bytes(dims, keep)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _lib.check("think_append_decode_attn", _lib.lib.think_append_decode_attn(
+        ctypes.byref(dims), _p(q), _p(k_new), _p(v_new), _p(k_thin), _p(v_cache), _p(seq_lens),
+        _p(kept_idx), int(keep), float(softmax_scale), _p(out), _p(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
 
 
 def think_k2_state_bytes(dims):

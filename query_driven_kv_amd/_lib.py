@@ -19,7 +19,8 @@ EXPORTS = ("think_abi_version", "think_keep_from_ratio", "think_score_workspace_
            "think_decode_workspace_bytes", "think_score", "think_score_select", "think_select",
            "think_compact_k",
            "think_decode_attn", "think_decode_attn_partial", "think_decode_attn_combine",
-           "think_append_kv", "think_k2_state_bytes", "think_prefill_write_kv",
+           "think_append_kv", "think_append_decode_attn", "think_k2_state_bytes",
+           "think_prefill_write_kv",
            "think_score_select_k2", "think_status_string", "think_last_hip_error")
 
 
@@ -67,6 +68,8 @@ def _load():
     l.think_decode_attn_partial.argtypes = [pd, vp, vp, vp, vp, vp, i32, ctypes.c_float, vp, sz, vp]
     l.think_decode_attn_combine.argtypes = [pd, vp, i32, vp, vp, sz, vp]
     l.think_append_kv.argtypes = [pd, vp, vp, vp, vp, i32, vp, vp, vp]
+    l.think_append_decode_attn.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, i32, ctypes.c_float, vp,
+                                           vp, sz, vp]
     l.think_k2_state_bytes.argtypes = [pd]
     l.think_k2_state_bytes.restype = sz
     l.think_prefill_write_kv.argtypes = [pd, vp, vp, i32, i32, vp, vp, vp, vp, sz, vp]
@@ -77,6 +80,7 @@ def _load():
     for name in ("think_score", "think_score_select", "think_select", "think_compact_k",
                  "think_decode_attn",
                  "think_decode_attn_partial", "think_decode_attn_combine", "think_append_kv",
+                 "think_append_decode_attn",
                  "think_prefill_write_kv", "think_score_select_k2"):
         getattr(l, name).restype = ctypes.c_int
     return l

@@ -29,7 +29,7 @@ int mfma_decode_chunk(const think_dims& d, int keep);
 hipError_t launch_decode_mfma(const think_dims& d, const DecodeGeom& g, const void* q,
                               const void* k_thin, const void* v_cache, const int32_t* seq_lens,
                               const int32_t* kept_idx, int keep, float scale, float* partials,
-                              hipStream_t s);
+                              int32_t* stash, hipStream_t s);
 
 namespace {
 
@@ -50,10 +50,12 @@ __global__ __launch_bounds__(kThreads) void k_decode_partial(
         const typename Elem<DT>::T* __restrict__ q, const typename Elem<DT>::T* __restrict__ k_thin,
         const typename Elem<DT>::T* __restrict__ v_cache, const int32_t* __restrict__ seq_lens,
         const int32_t* __restrict__ kept_idx, int s_cap, int Hkv, int G, int D, int keep,
-        float scale, int nsplit, int rec, float* __restrict__ partials) {
+        float scale, int nsplit, int rec, float* __restrict__ partials,
+        int32_t* __restrict__ stash) {
     using E = Elem<DT>;
     const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
     const int len = clamp_len(seq_lens, b, s_cap);
+    if (stash && split == 0 && kv == 0 && threadIdx.x == 0) stash[b] = len;   // fused append
     const int t0 = split * kChunk;
     if (t0 >= len) return;                       // the combine stops before this chunk
     const int nt = min(kChunk, len - t0);
@@ -140,11 +142,16 @@ __global__ __launch_bounds__(kThreads) void k_decode_partial(
 // load; slots at or past the sequence's chunk count are dropped after loading
 // (their contents are never used).  Balanced slots: every wave first derives
 // the sequence's slot range from all B lengths (balanced_slots), then loads.
+// Fused append (ap.stash set): the lengths are the ones the chunk pass
+// stashed; the new token, at position len_b below capacity, is merged last as
+// one more term (its logit from the kept channels of q and k_new, a fixed-
+// order sum, its value row v_new), then its thin key and value rows are
+// written and seq_lens[b] advanced (no workgroup of this grid reads seq_lens).
 template <int DT>
 __global__ __launch_bounds__(1024) void k_decode_combine(
         const float* __restrict__ partials, const int32_t* __restrict__ seq_lens, int s_cap,
         int chunk, int mode, int nsplit, int rec, int D, int sg_count,
-        typename Elem<DT>::T* __restrict__ out) {
+        typename Elem<DT>::T* __restrict__ out, AppendArgs ap) {
     using E = Elem<DT>;
     using MT = LogitT<DT>;
     constexpr MT kNone = -3.402823466e38f;      // finite stand-in for an empty maximum
@@ -153,12 +160,13 @@ __global__ __launch_bounds__(1024) void k_decode_combine(
     const int D4 = D >> 2;
     const int d4 = tid % D4, sg = tid / D4;
     const float* base = partials + ((size_t)b * Hq + h) * nsplit * rec;
+    const int32_t* lens = ap.stash ? ap.stash : seq_lens;
     int nrange = nsplit, used = 0;               // slots in the ranges; used: balanced only
     int len_raw = 0;
     if (mode == kBalanced) {
         const int lane = tid & 63;   // lanes past B read zero
         const int lr = __builtin_amdgcn_raw_buffer_load_b32(
-                make_rsrc(seq_lens, (uint32_t)nb * 4u), lane * 4, 0, 0);
+                make_rsrc(lens, (uint32_t)nb * 4u), lane * 4, 0, 0);
         const SeqSlots ss = balanced_slots(lr < 0 ? 0 : (lr > s_cap ? s_cap : lr), nsplit * nb,
                                            kDecodeUnit, kDecodeMinChunk);
         const int first = __builtin_amdgcn_readfirstlane(__shfl(ss.first, b));
@@ -166,7 +174,7 @@ __global__ __launch_bounds__(1024) void k_decode_combine(
         base = partials + ((size_t)h * nsplit * nb + first) * rec;
         nrange = used;
     } else {
-        len_raw = seq_lens[b];
+        len_raw = lens[b];
     }
     const int lo = (int)((unsigned)(sg * nrange) / (unsigned)sg_count);
     const int hi = (int)((unsigned)((sg + 1) * nrange) / (unsigned)sg_count);
@@ -228,12 +236,42 @@ __global__ __launch_bounds__(1024) void k_decode_combine(
     __shared__ MT sM[64];
     __shared__ float sL[64];
     __shared__ float4 sO[1024];
+    __shared__ MT s_prod[256], s_dot[4];
+    // fused append: the new token's logit, q . k_new over the kept channels
+    // (one product per channel, summed in channel order in four runs of 64,
+    // the runs added in order)
+    const int Hkv = ap.n_kv_heads, kv = h / (Hq / (Hkv > 0 ? Hkv : 1));
+    int lenb = 0;
+    bool app = false;
+    if (ap.stash) {
+        lenb = ap.stash[b];
+        app = lenb < s_cap;
+        const int32_t* idx = ap.kept_idx + ((size_t)b * Hkv + kv) * ap.keep;
+        for (int j = tid; j < 256; j += blockDim.x) {
+            MT prod = 0;
+            if (j < ap.keep) {
+                int c = idx[j];
+                c = c < 0 ? 0 : (c >= D ? D - 1 : c);
+                prod = (MT)E::load((const typename E::T*)ap.q, ((size_t)b * Hq + h) * D + c) *
+                       (MT)E::load((const typename E::T*)ap.k_new, ((size_t)b * Hkv + kv) * D + c);
+            }
+            s_prod[j] = prod;
+        }
+    }
     if (d4 == 0) {
         sM[sg] = M;
         sL[sg] = L;
     }
     sO[tid] = O;
     __syncthreads();
+    if (ap.stash) {                              // uniform: a kernel argument
+        if (tid < 4) {
+            MT t = 0;
+            for (int i = 0; i < 64; ++i) t += s_prod[tid * 64 + i];
+            s_dot[tid] = t;
+        }
+        __syncthreads();
+    }
     if (sg == 0) {
         MT MM = sM[0];
         for (int r = 1; r < sg_count; ++r) MM = sM[r] > MM ? sM[r] : MM;
@@ -248,12 +286,44 @@ __global__ __launch_bounds__(1024) void k_decode_combine(
             OO.z = fmaf(f, o.z, OO.z);
             OO.w = fmaf(f, o.w, OO.w);
         }
+        if (app) {
+            const MT lnew = (((s_dot[0] + s_dot[1]) + s_dot[2]) + s_dot[3]) * (MT)ap.scale;
+            const MT Mf = lnew > MM ? lnew : MM;
+            const float a = LL > 0.0f ? expf((float)(MM - Mf)) : 0.0f;
+            const float wn = expf((float)(lnew - Mf));
+            const size_t v0 = ((size_t)b * Hkv + kv) * D + 4 * d4;
+            const typename E::T* vn = (const typename E::T*)ap.v_new;
+            LL = fmaf(LL, a, wn);
+            OO.x = fmaf(OO.x, a, wn * E::load(vn, v0 + 0));
+            OO.y = fmaf(OO.y, a, wn * E::load(vn, v0 + 1));
+            OO.z = fmaf(OO.z, a, wn * E::load(vn, v0 + 2));
+            OO.w = fmaf(OO.w, a, wn * E::load(vn, v0 + 3));
+        }
         const bool any = LL > 0.0f;
         const size_t o0 = ((size_t)b * Hq + h) * D + 4 * d4;
         E::store(out, o0 + 0, any ? OO.x / LL : 0.0f);
         E::store(out, o0 + 1, any ? OO.y / LL : 0.0f);
         E::store(out, o0 + 2, any ? OO.z / LL : 0.0f);
         E::store(out, o0 + 3, any ? OO.w / LL : 0.0f);
+    }
+    // fused append: the new token's rows (one workgroup per kv head) and the
+    // advanced length
+    if (app) {
+        using T = typename E::T;
+        if (h % (Hq / Hkv) == 0) {
+            const int32_t* idx = ap.kept_idx + ((size_t)b * Hkv + kv) * ap.keep;
+            const T* kn = (const T*)ap.k_new + ((size_t)b * Hkv + kv) * D;
+            T* kt = (T*)ap.k_thin + (((size_t)b * s_cap + lenb) * Hkv + kv) * ap.keep;
+            for (int j = tid; j < ap.keep; j += blockDim.x) {
+                int c = idx[j];
+                c = c < 0 ? 0 : (c >= D ? D - 1 : c);
+                kt[j] = kn[c];
+            }
+            const T* vn = (const T*)ap.v_new + ((size_t)b * Hkv + kv) * D;
+            T* vr = (T*)ap.v_cache + (((size_t)b * s_cap + lenb) * Hkv + kv) * D;
+            for (int e = tid; e < D; e += blockDim.x) vr[e] = vn[e];
+        }
+        if (h == 0 && tid == 0) ap.seq_lens[b] = lenb + 1;
     }
 }
 
@@ -266,33 +336,38 @@ DecodeGeom decode_geom(const think_dims& d, int keep) {
     g.chunk = g.mfma ? mfma_decode_chunk(d, keep) : kChunk;
     g.nsplit = (d.seq_capacity + g.chunk - 1) / g.chunk;
     g.rec = d.head_dim + 4;
-    g.ws_bytes = (size_t)d.batch * d.n_q_heads * g.nsplit * g.rec * sizeof(float);
+    g.stash_offset = (size_t)d.batch * d.n_q_heads * g.nsplit * g.rec * sizeof(float);
+    g.ws_bytes = g.stash_offset + ((size_t)d.batch * sizeof(int32_t) + 15) / 16 * 16;
     return g;
 }
 
 hipError_t launch_decode_partial(const think_dims& d, const DecodeGeom& g, const void* q,
                                  const void* k_thin, const void* v_cache, const int32_t* seq_lens,
                                  const int32_t* kept_idx, int keep, float scale, float* partials,
-                                 hipStream_t s) {
+                                 int32_t* stash, hipStream_t s) {
     if (g.mfma)
         return launch_decode_mfma(d, g, q, k_thin, v_cache, seq_lens, kept_idx, keep, scale,
-                                  partials, s);
+                                  partials, stash, s);
     const int G = d.n_q_heads / d.n_kv_heads;
     dim3 grid(g.nsplit, d.n_kv_heads, d.batch);
     if (d.dtype == THINK_BF16)
         k_decode_partial<THINK_BF16><<<grid, kThreads, 0, s>>>(
             (const uint16_t*)q, (const uint16_t*)k_thin, (const uint16_t*)v_cache, seq_lens,
             kept_idx, d.seq_capacity, d.n_kv_heads, G, d.head_dim, keep, scale, g.nsplit, g.rec,
-            partials);
+            partials, stash);
     else
         k_decode_partial<THINK_F32><<<grid, kThreads, 0, s>>>(
             (const float*)q, (const float*)k_thin, (const float*)v_cache, seq_lens, kept_idx,
-            d.seq_capacity, d.n_kv_heads, G, d.head_dim, keep, scale, g.nsplit, g.rec, partials);
+            d.seq_capacity, d.n_kv_heads, G, d.head_dim, keep, scale, g.nsplit, g.rec, partials,
+            stash);
     return hipGetLastError();
 }
 
 hipError_t launch_decode_combine(const think_dims& d, const DecodeGeom& g, const int32_t* seq_lens,
-                                 void* out, const float* partials, hipStream_t s) {
+                                 void* out, const float* partials, const AppendArgs* app,
+                                 hipStream_t s) {
+    AppendArgs ap{};
+    if (app) ap = *app;
     dim3 cgrid(d.n_q_heads, d.batch);
     int sg_count = 1024 / d.head_dim;
     if (sg_count > 16) sg_count = 16;
@@ -300,11 +375,11 @@ hipError_t launch_decode_combine(const think_dims& d, const DecodeGeom& g, const
     if (d.dtype == THINK_BF16)
         k_decode_combine<THINK_BF16><<<cgrid, cthreads, 0, s>>>(
             partials, seq_lens, d.seq_capacity, g.chunk, g.mode, g.nsplit, g.rec, d.head_dim,
-            sg_count, (uint16_t*)out);
+            sg_count, (uint16_t*)out, ap);
     else
         k_decode_combine<THINK_F32><<<cgrid, cthreads, 0, s>>>(
             partials, seq_lens, d.seq_capacity, g.chunk, g.mode, g.nsplit, g.rec, d.head_dim,
-            sg_count, (float*)out);
+            sg_count, (float*)out, ap);
     return hipGetLastError();
 }
 

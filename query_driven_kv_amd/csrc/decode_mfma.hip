@@ -293,9 +293,16 @@ __global__ __launch_bounds__(kThreads, (KAL == 8 && KB <= 2) ? 3 : 2) void k_dec
         const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_thin,
         const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ seq_lens,
         const int32_t* __restrict__ kept_idx, int s_cap, int Hkv, int G, int keep, float scale,
-        int chunk, int nsplit, int rec, int mode, float* __restrict__ partials) {
+        int chunk, int nsplit, int rec, int mode, float* __restrict__ partials,
+        int32_t* __restrict__ stash) {
     const int split = blockIdx.x, kv = blockIdx.y;
     const int tid = threadIdx.x;
+    // fused append: the first workgroup of each sequence records the length
+    // this pass reads, for the combine (which then advances seq_lens)
+    if (stash && split == 0 && kv == 0 && tid == 0) {
+        const int n = seq_lens[blockIdx.z];
+        stash[blockIdx.z] = n < 0 ? 0 : (n > s_cap ? s_cap : n);
+    }
     const int Hq = Hkv * G;
     const int lane = tid & 63, wave = tid >> 6;
     const int n16 = lane & 15, q4 = lane >> 4;
@@ -489,13 +496,13 @@ template <int KB>
 hipError_t launch_kb(int kal, dim3 grid, hipStream_t s, const uint16_t* q, const uint16_t* kt,
                      const uint16_t* v, const int32_t* lens, const int32_t* idx, int s_cap,
                      int Hkv, int G, int keep, float scale, int chunk, int nsplit, int rec,
-                     int mode, float* part) {
+                     int mode, float* part, int32_t* stash) {
     if (kal == 8)
         k_decode_mfma<KB, 8><<<grid, kThreads, 0, s>>>(q, kt, v, lens, idx, s_cap, Hkv, G, keep,
-                                                       scale, chunk, nsplit, rec, mode, part);
+                                                       scale, chunk, nsplit, rec, mode, part, stash);
     else
         k_decode_mfma<KB, 0><<<grid, kThreads, 0, s>>>(q, kt, v, lens, idx, s_cap, Hkv, G, keep,
-                                                       scale, chunk, nsplit, rec, mode, part);
+                                                       scale, chunk, nsplit, rec, mode, part, stash);
     return hipGetLastError();
 }
 
@@ -529,7 +536,7 @@ int mfma_decode_chunk(const think_dims& d, int keep) {
 hipError_t launch_decode_mfma(const think_dims& d, const DecodeGeom& g, const void* q,
                               const void* k_thin, const void* v_cache, const int32_t* seq_lens,
                               const int32_t* kept_idx, int keep, float scale, float* partials,
-                              hipStream_t s) {
+                              int32_t* stash, hipStream_t s) {
     const int G = d.n_q_heads / d.n_kv_heads;
     const int kal = keep % 8 == 0 ? 8 : 0;
     const int KB = (keep + 31) / 32;
@@ -540,7 +547,7 @@ hipError_t launch_decode_mfma(const think_dims& d, const DecodeGeom& g, const vo
     auto go = [&](auto kb) {
         return launch_kb<decltype(kb)::value>(kal, grid, s, qp, kp, vp, seq_lens, kept_idx,
                                               d.seq_capacity, d.n_kv_heads, G, keep, scale,
-                                              g.chunk, g.nsplit, g.rec, g.mode, partials);
+                                              g.chunk, g.nsplit, g.rec, g.mode, partials, stash);
     };
     switch (KB) {
         case 1: return go(std::integral_constant<int, 1>{});

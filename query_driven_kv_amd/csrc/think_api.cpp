@@ -124,15 +124,18 @@ namespace {
 int check_decode(const think_dims* d, const void* q, const void* k_thin, const void* v_cache,
                  const int32_t* seq_lens, const int32_t* kept_idx, bool need_inputs,
                  const void* out, bool need_out, int32_t keep, const void* workspace,
-                 size_t workspace_bytes, thinkkv::DecodeGeom* g) {
+                 size_t workspace_bytes, thinkkv::DecodeGeom* g, bool need_new = false,
+                 const void* k_new = nullptr, const void* v_new = nullptr) {
     int st = check_dims(d);
     if (st != THINK_OK) return st;
     if (!seq_lens) return THINK_ERR_NULL;
     if (need_inputs && (!q || !k_thin || !v_cache || !kept_idx)) return THINK_ERR_NULL;
     if (need_out && !out) return THINK_ERR_NULL;
+    if (need_new && (!k_new || !v_new)) return THINK_ERR_NULL;
     if (keep < 1 || keep > d->head_dim) return THINK_ERR_KEEP;
     if (need_inputs && (!aligned16(k_thin) || !aligned16(v_cache) || !aligned16(q)))
         return THINK_ERR_UNSUPPORTED;
+    if (need_new && (!aligned16(k_new) || !aligned16(v_new))) return THINK_ERR_UNSUPPORTED;
     *g = thinkkv::decode_geom(*d, keep);
     if (!workspace || workspace_bytes < g->ws_bytes || !aligned16(workspace))
         return THINK_ERR_WORKSPACE;
@@ -151,10 +154,10 @@ int think_decode_attn(const think_dims* d, const void* q, const void* k_thin,
     if (st != THINK_OK) return st;
     st = hip_status(thinkkv::launch_decode_partial(*d, g, q, k_thin, v_cache, seq_lens, kept_idx,
                                                    keep, softmax_scale, (float*)workspace,
-                                                   (hipStream_t)stream));
+                                                   nullptr, (hipStream_t)stream));
     if (st != THINK_OK) return st;
     return hip_status(thinkkv::launch_decode_combine(*d, g, seq_lens, out, (const float*)workspace,
-                                                     (hipStream_t)stream));
+                                                     nullptr, (hipStream_t)stream));
 }
 
 int think_decode_attn_partial(const think_dims* d, const void* q, const void* k_thin,
@@ -167,7 +170,7 @@ int think_decode_attn_partial(const think_dims* d, const void* q, const void* k_
     if (st != THINK_OK) return st;
     return hip_status(thinkkv::launch_decode_partial(*d, g, q, k_thin, v_cache, seq_lens, kept_idx,
                                                      keep, softmax_scale, (float*)workspace,
-                                                     (hipStream_t)stream));
+                                                     nullptr, (hipStream_t)stream));
 }
 
 int think_decode_attn_combine(const think_dims* d, const int32_t* seq_lens, int32_t keep,
@@ -178,7 +181,7 @@ int think_decode_attn_combine(const think_dims* d, const int32_t* seq_lens, int3
                           workspace, workspace_bytes, &g);
     if (st != THINK_OK) return st;
     return hip_status(thinkkv::launch_decode_combine(*d, g, seq_lens, out, (const float*)workspace,
-                                                     (hipStream_t)stream));
+                                                     nullptr, (hipStream_t)stream));
 }
 
 int think_append_kv(const think_dims* d, const void* k_new, const void* v_new, int32_t* seq_lens,
@@ -192,6 +195,25 @@ int think_append_kv(const think_dims* d, const void* k_new, const void* v_new, i
         return THINK_ERR_UNSUPPORTED;
     return hip_status(thinkkv::launch_append(*d, k_new, v_new, seq_lens, kept_idx, keep, k_thin,
                                              v_cache, (hipStream_t)stream));
+}
+
+int think_append_decode_attn(const think_dims* d, const void* q, const void* k_new,
+                             const void* v_new, void* k_thin, void* v_cache, int32_t* seq_lens,
+                             const int32_t* kept_idx, int32_t keep, float softmax_scale,
+                             void* out, void* workspace, size_t workspace_bytes, void* stream) {
+    thinkkv::DecodeGeom g;
+    int st = check_decode(d, q, k_thin, v_cache, seq_lens, kept_idx, true, out, true, keep,
+                          workspace, workspace_bytes, &g, true, k_new, v_new);
+    if (st != THINK_OK) return st;
+    int32_t* stash = (int32_t*)((char*)workspace + g.stash_offset);
+    st = hip_status(thinkkv::launch_decode_partial(*d, g, q, k_thin, v_cache, seq_lens, kept_idx,
+                                                   keep, softmax_scale, (float*)workspace, stash,
+                                                   (hipStream_t)stream));
+    if (st != THINK_OK) return st;
+    thinkkv::AppendArgs ap{q, k_new, v_new, kept_idx, k_thin, v_cache, seq_lens, stash, keep,
+                           d->n_kv_heads, softmax_scale};
+    return hip_status(thinkkv::launch_decode_combine(*d, g, seq_lens, out, (const float*)workspace,
+                                                     &ap, (hipStream_t)stream));
 }
 
 size_t think_k2_state_bytes(const think_dims* d) {

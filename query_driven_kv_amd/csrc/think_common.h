@@ -175,9 +175,28 @@ struct DecodeGeom {
     int rec;          // floats per partial record: m, l, 2 pad, o[D]
     bool mfma;        // bf16 matrix-core kernel
     int mode;         // DecodeMode
-    size_t ws_bytes;  // B * Hq * nsplit records of rec fp32
+    size_t stash_offset;  // byte offset of the lengths the chunk pass used (fused append)
+    size_t ws_bytes;  // B * Hq * nsplit records of rec fp32, then B int32 lengths
 };
 DecodeGeom decode_geom(const think_dims& d, int keep);
+
+// Decode-time append fused into the decode (think_append_decode_attn): the
+// chunk pass attends over the cached tokens and stashes the lengths it used;
+// the combine adds the new token as one more softmax term, writes its rows
+// into the caches and advances the lengths.
+struct AppendArgs {
+    const void* q;             // [B, Hq, D]
+    const void* k_new;         // [B, Hkv, D]
+    const void* v_new;         // [B, Hkv, D]
+    const int32_t* kept_idx;   // [B, Hkv, keep]
+    void* k_thin;              // [B, S_cap, Hkv, keep], row len_b written
+    void* v_cache;             // [B, S_cap, Hkv, D], row len_b written
+    int32_t* seq_lens;         // advanced to len_b + 1 (below capacity)
+    const int32_t* stash;      // the lengths the chunk pass read
+    int keep;
+    int n_kv_heads;
+    float scale;
+};
 
 // Prefill-write state: fp64 sums of squares per (b, slot, channel).
 struct K2Geom {
@@ -215,11 +234,14 @@ hipError_t launch_score_k2(const think_dims& d, int nslots, const double* state,
 hipError_t launch_append(const think_dims& d, const void* k_new, const void* v_new,
                          int32_t* seq_lens, const int32_t* kept_idx, int keep, void* k_thin,
                          void* v_cache, hipStream_t s);
+// stash: NULL, or where the chunk pass stores the lengths it read (fused append)
 hipError_t launch_decode_partial(const think_dims& d, const DecodeGeom& g, const void* q,
                                  const void* k_thin, const void* v_cache, const int32_t* seq_lens,
                                  const int32_t* kept_idx, int keep, float scale, float* partials,
-                                 hipStream_t s);
+                                 int32_t* stash, hipStream_t s);
+// app: NULL, or the fused append (its stash replaces seq_lens as the lengths)
 hipError_t launch_decode_combine(const think_dims& d, const DecodeGeom& g, const int32_t* seq_lens,
-                                 void* out, const float* partials, hipStream_t s);
+                                 void* out, const float* partials, const AppendArgs* app,
+                                 hipStream_t s);
 
 }  // namespace thinkkv

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_header_declarations_are_all_exported(L):
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     assert sorted(L.EXPORTS) == names
     so = ctypes.CDLL(L.LIB_PATH)
     for n in names:
@@ -42,7 +42,7 @@ def test_only_the_abi_is_exported(L):
 
 def test_version_and_keep_rounding(L):
     lib = L.lib
-    assert lib.think_abi_version() == 3
+    assert lib.think_abi_version() == 4
     assert [lib.think_keep_from_ratio(128, r) for r in (0.4, 0.6, 0.5)] == [77, 51, 64]
     assert lib.think_keep_from_ratio(16, 0.5) == 8
     assert lib.think_keep_from_ratio(128, 0.0) == 128
@@ -145,6 +145,33 @@ def test_append_validation(L):
     odd = ctypes.c_void_p(0x100008)
     assert lib.think_append_kv(ctypes.byref(d), odd, FAKE, FAKE, FAKE, 8, FAKE, FAKE, None) == -5
     assert lib.think_append_kv(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 8, FAKE, odd, None) == -5
+
+
+def test_append_decode_validation(L):
+    lib = L.lib
+    d = dims(L)
+    big = 1 << 30
+    f = lib.think_append_decode_attn
+    # q, k_new, v_new, k_thin, v_cache, seq_lens, kept_idx, keep, scale, out, ws, bytes, stream
+    assert f(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 0.1, FAKE, FAKE, big, None) == -1
+    for i in range(7):                                   # each required pointer but the workspace
+        args = [FAKE] * 7
+        args[i] = None
+        q, kn, vn, kt, vc, lens, idx = args
+        assert f(ctypes.byref(d), q, kn, vn, kt, vc, lens, idx, 8, 0.1, FAKE, FAKE, big,
+                 None) == -1, i
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 0.1, None, FAKE, big,
+             None) == -1
+    for keep in (0, 129):
+        assert f(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, keep, 0.1, FAKE, FAKE,
+                 big, None) == -3
+    odd = ctypes.c_void_p(0x100008)
+    assert f(ctypes.byref(d), FAKE, odd, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 0.1, FAKE, FAKE, big,
+             None) == -5
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 0.1, FAKE, FAKE, 16,
+             None) == -6
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 0.1, FAKE, None, big,
+             None) == -6
 
 
 def test_null_keep_window_workspace_and_alignment(L):

@@ -1,10 +1,13 @@
-"""GPU parity of the decode-time append against the oracle: think_append_kv
-then think_decode_attn, several steps in a row, on the same seeded inputs.
-The thin-key and value caches and the lengths must match the oracle's byte
-for byte after every step (the padding beyond the new length still holds the
-NaN sentinel), and the attention over len_b + 1 tokens must be within the
-decode tolerance.  Cases cover ragged batches, odd keep, fp32, a sequence that
-fills its last slot and one already at capacity (left as it is)."""
+"""GPU parity of the decode-time append against the oracle, several steps in
+a row on the same seeded inputs: think_append_kv then think_decode_attn, and
+the fused think_append_decode_attn (the append folded into the decode's
+merge).  The thin-key and value caches and the lengths must match the
+oracle's byte for byte after every step (the padding beyond the new length
+still holds the NaN sentinel), and the attention over len_b + 1 tokens must be
+within the decode tolerance.  Cases cover ragged batches (chunk slots dealt by
+length), one long sequence, batches past the balanced range, odd keep, fp32,
+empty sequences, a sequence that fills its last slot and one already at
+capacity (left as it is, attending over its cached tokens only)."""
 import numpy as np
 import pytest
 import torch
@@ -21,29 +24,41 @@ CASES = [
     (51, [1000, 998], 4, 1, 128, 1000, 51, "bf16"),        # odd keep; one sequence full
     (52, [63, 40], 6, 3, 64, 66, 20, "f32"),               # general decode, fp32
     (53, [5, 2047], 32, 8, 128, 2048, 77, "bf16"),         # slot S_cap-1 filled by the first step
+    (54, [0, 700, 0, 33], 8, 2, 128, 1024, 32, "bf16"),   # empty sequences
+    (55, [9000], 32, 8, 128, 9216, 64, "bf16"),            # one long sequence
+    (56, [0, 130], 4, 2, 32, 160, 9, "f32"),               # general decode, empty sequence
+    (57, [(37 * i) % 300 for i in range(70)], 8, 2, 128, 300, 40, "bf16"),  # B past 64
+    (58, [2, 1], 4, 1, 64, 2, 16, "bf16"),                 # capacity 2: both full by step 2
 ]
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
 @pytest.mark.parametrize("case", CASES, ids=[f"append{c[0]}" for c in CASES])
-def test_append_then_decode(case):
+def test_append_then_decode(case, fused):
     import query_driven_kv_amd as qdk
     seed, lens, Hq, Hkv, D, S, keep, dtype = case
     B = len(lens)
-    print(f"[append] seed {seed}: B={B} S={S} Hq={Hq} Hkv={Hkv} D={D} keep={keep} {dtype}",
-          flush=True)
+    print(f"[append] seed {seed} fused={fused}: B={B} S={S} Hq={Hq} Hkv={Hkv} D={D} "
+          f"keep={keep} {dtype}", flush=True)
     cfg = kvsynth.custom(f"append{seed}", batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D,
                          seq_capacity=S, obs_window=4, keep=keep, dtype=dtype, cfg_id=91,
                          lowrank=8 if D >= 64 else 0)
     L = kvsynth.make_layer(cfg, layer=seed)
     lens = np.asarray(lens, np.int32)
     nan = kvsynth.nan_value(dtype)
+    # an empty sequence takes its channel set from the one token the cache
+    # held before it was emptied; its row 0 is padding again afterwards
+    lens_sel = np.maximum(lens, 1)
     for b in range(B):
-        L["k_cache"][b, lens[b]:] = nan
-        L["v_cache"][b, lens[b]:] = nan
-    s = oracle.score(L["k_cache"], lens, L["q_obs"])
+        L["k_cache"][b, lens_sel[b]:] = nan
+        L["v_cache"][b, lens_sel[b]:] = nan
+    s = oracle.score(L["k_cache"], lens_sel, L["q_obs"])
     idx, _ = oracle.select(s, keep)
-    thin = oracle.compact(L["k_cache"], lens, idx, fill=nan)
+    thin = oracle.compact(L["k_cache"], lens_sel, idx, fill=nan)
     v = L["v_cache"]
+    for b in np.flatnonzero(lens == 0):
+        thin[b, 0] = nan
+        v[b, 0] = nan
     scale = np.float32(1.0 / np.sqrt(D))
 
     thin_d, v_d, lens_d, idx_d = to_dev(thin), to_dev(v), to_dev(lens), to_dev(idx)
@@ -51,8 +66,12 @@ def test_append_then_decode(case):
     for step in range(3):
         k_new, v_new = kvsynth.decode_kv(cfg, seed, step, L["channel_scale"])
         q = kvsynth.decode_q(cfg, seed, step, L["channel_scale"])
-        qdk.think_append_kv(to_dev(k_new), to_dev(v_new), lens_d, idx_d, thin_d, v_d)
-        out = qdk.think_decode_attn(to_dev(q), thin_d, v_d, lens_d, idx_d, scale)
+        if fused:
+            out = qdk.think_append_decode_attn(to_dev(q), to_dev(k_new), to_dev(v_new), thin_d,
+                                               v_d, lens_d, idx_d, scale)
+        else:
+            qdk.think_append_kv(to_dev(k_new), to_dev(v_new), lens_d, idx_d, thin_d, v_d)
+            out = qdk.think_decode_attn(to_dev(q), thin_d, v_d, lens_d, idx_d, scale)
         torch.cuda.synchronize()
         o_thin, o_v, o_lens = oracle.append(k_new, v_new, o_lens, idx, o_thin, o_v)
         np.testing.assert_array_equal(to_host(lens_d), o_lens)
