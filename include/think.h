@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define THINK_ABI_VERSION 4
+#define THINK_ABI_VERSION 5
 
 #ifndef THINK_API
 #define THINK_API __attribute__((visibility("default")))
@@ -144,6 +144,36 @@ THINK_API int think_score_select(const think_dims *d, const void *k_cache, const
  */
 THINK_API int think_compact_k(const think_dims *d, const void *k_cache, const int32_t *seq_lens,
                     const int32_t *kept_idx, int32_t keep, void *k_thin, void *stream);
+
+/*
+ * Stages (a) + (b) + (c) in one call ("ThinK", Technical framework: score,
+ * prune, store the pruned key cache).  Same arguments and outputs as
+ * think_score_select followed by think_compact_k; scores and near_tie may be
+ * NULL.  When the key cache fits in the device's register files (by capacity:
+ * up to 256 KiB per compute unit, 64 MiB on a 256-CU part; the exact rule is
+ * think_score_compact_single_read), one launch of one workgroup per compute
+ * unit reads K once, holds it on chip while the channels are selected and
+ * writes k_thin from there; otherwise the two-pass kernels run.  The
+ * workgroups of that launch wait for one another (bounded waits), so it
+ * should not share the device with a kernel that never finishes.
+ * Both paths give the same kept channels up to the near-tie flag (scores may
+ * differ in the last fp32 place: the token sums are split differently) and,
+ * for the same kept channels, the same k_thin bytes.
+ *   workspace   >= think_score_compact_workspace_bytes(d, keep) bytes, 16-byte
+ *               aligned, any previous contents (the single-read launch keeps
+ *               a barrier counter there, tagged per launch; calls that share a
+ *               workspace must not overlap in time)
+ */
+THINK_API int think_score_select_compact(const think_dims *d, const void *k_cache,
+                                         const int32_t *seq_lens, const void *q_obs,
+                                         int32_t obs_window, int32_t keep, float *scores,
+                                         int32_t *kept_idx, int32_t *near_tie, void *k_thin,
+                                         void *workspace, size_t workspace_bytes, void *stream);
+THINK_API size_t think_score_compact_workspace_bytes(const think_dims *d, int32_t keep);
+/* 1 if think_score_select_compact takes the single-read launch for this shape
+ * on the current device, 0 if it runs the two-pass kernels, negative status
+ * for invalid dims or keep. */
+THINK_API int think_score_compact_single_read(const think_dims *d, int32_t keep);
 
 /*
  * Stage (d) - one decode step of attention on the pruned keys ("ThinK",

@@ -21,6 +21,8 @@ __all__ = ["think_score", "think_score_select", "think_select", "think_compact_k
            "think_decode_attn",
            "think_decode_attn_partial", "think_decode_attn_combine", "think_append_kv",
            "think_append_decode_attn", "think_k2_state_bytes", "think_prefill_write_kv", "think_score_select_k2",
+           "think_score_select_compact", "think_score_compact_workspace_bytes",
+           "think_score_compact_single_read",
            "think_keep_from_ratio", "think_score_workspace_bytes", "think_decode_workspace_bytes",
            "think_abi_version", "make_dims", "ThinkError", "think_dims", "LIB_PATH"]
 
@@ -72,6 +74,19 @@ def think_score_workspace_bytes(dims):
 
 def think_decode_workspace_bytes(dims, keep):
     return _lib.lib.think_decode_workspace_bytes(ctypes.byref(dims), int(keep))
+
+
+def think_score_compact_workspace_bytes(dims, keep):
+    return _lib.lib.think_score_compact_workspace_bytes(ctypes.byref(dims), int(keep))
+
+
+def think_score_compact_single_read(dims, keep):
+    """1: think_score_select_compact reads K once for this shape on the current
+    device; 0: it runs the two-pass kernels."""
+    r = _lib.lib.think_score_compact_single_read(ctypes.byref(dims), int(keep))
+    if r < 0:
+        _lib.check("think_score_compact_single_read", r)
+    return r
 
 
 def _i32(t, name):
@@ -165,6 +180,40 @@ def think_compact_k(k_cache, seq_lens, kept_idx, *, k_thin=None, stream=None):
         ctypes.byref(dims), _p(k_cache), _p(seq_lens), _p(kept_idx), keep, _p(k_thin),
         _stream(stream)))
     return k_thin
+
+
+def think_score_select_compact(k_cache, seq_lens, q_obs, keep, *, scores=None, kept_idx=None,
+                               near_tie=None, k_thin=None, workspace=None, stream=None):
+    """Stages (a)+(b)+(c) in one call (one read of K when it fits on chip).
+    Returns (scores fp32 [B,Hkv,D], kept_idx int32 [B,Hkv,keep], near_tie
+    int32 [B,Hkv], k_thin [B,S_cap,Hkv,keep])."""
+    _dev(k_cache, seq_lens, q_obs, scores, kept_idx, near_tie, k_thin, workspace)
+    _i32(seq_lens, "seq_lens")
+    B, S, Hkv, D = k_cache.shape
+    Bq, W, Hq, Dq = q_obs.shape
+    if (Bq, Dq) != (B, D) or q_obs.dtype != k_cache.dtype or tuple(seq_lens.shape) != (B,):
+        raise ValueError("shape or dtype mismatch between k_cache, q_obs and seq_lens")
+    dims = make_dims(B, Hq, Hkv, D, S, _dtype_code(k_cache))
+    dev = k_cache.device
+    keep = int(keep)
+    if scores is None:
+        scores = torch.empty(B, Hkv, D, dtype=torch.float32, device=dev)
+    if kept_idx is None:
+        kept_idx = torch.empty(B, Hkv, max(keep, 0), dtype=torch.int32, device=dev)
+    if near_tie is None:
+        near_tie = torch.empty(B, Hkv, dtype=torch.int32, device=dev)
+    if k_thin is None:
+        k_thin = torch.empty(B, S, Hkv, max(keep, 0), dtype=k_cache.dtype, device=dev)
+    elif tuple(k_thin.shape) != (B, S, Hkv, keep) or k_thin.dtype != k_cache.dtype:
+        raise ValueError("k_thin must be [B,S_cap,Hkv,keep] of the cache dtype")
+    if workspace is None:
+        workspace = torch.empty(max(think_score_compact_workspace_bytes(dims, keep), 16),
+                                dtype=torch.uint8, device=dev)
+    _lib.check("think_score_select_compact", _lib.lib.think_score_select_compact(
+        ctypes.byref(dims), _p(k_cache), _p(seq_lens), _p(q_obs), W, keep, _p(scores),
+        _p(kept_idx), _p(near_tie), _p(k_thin), _p(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return scores, kept_idx, near_tie, k_thin
 
 
 def think_decode_attn(q, k_thin, v_cache, seq_lens, kept_idx, softmax_scale, *, out=None,

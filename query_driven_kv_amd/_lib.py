@@ -21,7 +21,9 @@ EXPORTS = ("think_abi_version", "think_keep_from_ratio", "think_score_workspace_
            "think_decode_attn", "think_decode_attn_partial", "think_decode_attn_combine",
            "think_append_kv", "think_append_decode_attn", "think_k2_state_bytes",
            "think_prefill_write_kv",
-           "think_score_select_k2", "think_status_string", "think_last_hip_error")
+           "think_score_select_k2", "think_score_select_compact",
+           "think_score_compact_workspace_bytes", "think_score_compact_single_read",
+           "think_status_string", "think_last_hip_error")
 
 
 class think_dims(ctypes.Structure):
@@ -74,6 +76,11 @@ def _load():
     l.think_k2_state_bytes.restype = sz
     l.think_prefill_write_kv.argtypes = [pd, vp, vp, i32, i32, vp, vp, vp, vp, sz, vp]
     l.think_score_select_k2.argtypes = [pd, vp, sz, vp, i32, i32, vp, vp, vp, vp]
+    l.think_score_select_compact.argtypes = [pd, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    l.think_score_compact_workspace_bytes.argtypes = [pd, i32]
+    l.think_score_compact_workspace_bytes.restype = sz
+    l.think_score_compact_single_read.argtypes = [pd, i32]
+    l.think_score_compact_single_read.restype = ctypes.c_int
     l.think_status_string.argtypes = [ctypes.c_int]
     l.think_status_string.restype = ctypes.c_char_p
     l.think_last_hip_error.restype = ctypes.c_int
@@ -81,7 +88,7 @@ def _load():
                  "think_decode_attn",
                  "think_decode_attn_partial", "think_decode_attn_combine", "think_append_kv",
                  "think_append_decode_attn",
-                 "think_prefill_write_kv", "think_score_select_k2"):
+                 "think_prefill_write_kv", "think_score_select_k2", "think_score_select_compact"):
         getattr(l, name).restype = ctypes.c_int
     return l
 

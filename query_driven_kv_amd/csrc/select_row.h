@@ -19,10 +19,12 @@ namespace thinkkv {
 // as one 16-byte LDS load each, so the reads pipeline) and their partial
 // counts are added in a fixed order.  Ranks form a permutation, so no sort is
 // needed; the output slot of a kept channel (ascending order) comes from wave
-// ballots and prefix popcounts.
+// ballots and prefix popcounts.  mask_out (LDS, ceil(D/32) words, optional)
+// receives the kept set as a bit mask, bit c of word c/32 for channel c.
 __device__ __forceinline__ void select_row(const float* s, int D, int keep, int* scratch,
                                            float* cut, int32_t* __restrict__ idx_out,
-                                           int32_t* __restrict__ tie_out) {
+                                           int32_t* __restrict__ tie_out,
+                                           uint32_t* mask_out = nullptr) {
     const int tid = threadIdx.x, nth = blockDim.x;
     int parts = nth / D;
     if (parts > 16) parts = 16;
@@ -59,6 +61,10 @@ __device__ __forceinline__ void select_row(const float* s, int D, int keep, int*
     const int lane = tid & 63, wave = tid >> 6;
     const unsigned long long m = __ballot(take);
     if (lane == 0 && wave < 16) wave_kept[wave] = __popcll(m);
+    if (mask_out && lane == 0 && wave * 64 < D) {
+        mask_out[2 * wave] = (uint32_t)m;
+        if (wave * 64 + 32 < D) mask_out[2 * wave + 1] = (uint32_t)(m >> 32);
+    }
     __syncthreads();
     if (take) {
         int pos = __popcll(m & ((1ull << lane) - 1ull));

@@ -117,6 +117,53 @@ int think_compact_k(const think_dims* d, const void* k_cache, const int32_t* seq
                                               (hipStream_t)stream));
 }
 
+size_t think_score_compact_workspace_bytes(const think_dims* d, int32_t keep) {
+    if (check_dims(d) != THINK_OK || keep < 1 || keep > d->head_dim) return 0;
+    const size_t a = thinkkv::score_geom(*d).ws_bytes;
+    const size_t b = thinkkv::single_read_geom(*d, keep).ws_bytes;
+    return a > b ? a : b;
+}
+
+int think_score_compact_single_read(const think_dims* d, int32_t keep) {
+    int st = check_dims(d);
+    if (st != THINK_OK) return st;
+    if (keep < 1 || keep > d->head_dim) return THINK_ERR_KEEP;
+    thinkkv::SrPlan pl;
+    return thinkkv::single_read_plan(*d, keep, thinkkv::single_read_geom(*d, keep), &pl) ? 1 : 0;
+}
+
+int think_score_select_compact(const think_dims* d, const void* k_cache, const int32_t* seq_lens,
+                               const void* q_obs, int32_t obs_window, int32_t keep,
+                               float* scores, int32_t* kept_idx, int32_t* near_tie,
+                               void* k_thin, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    int st = check_dims(d);
+    if (st != THINK_OK) return st;
+    if (!k_cache || !seq_lens || !q_obs || !kept_idx || !k_thin) return THINK_ERR_NULL;
+    if (obs_window < 1) return THINK_ERR_SHAPE;
+    if (keep < 1 || keep > d->head_dim) return THINK_ERR_KEEP;
+    if (!aligned16(k_cache) || !aligned16(q_obs) || !aligned16(k_thin))
+        return THINK_ERR_UNSUPPORTED;
+    const thinkkv::SingleReadGeom sg = thinkkv::single_read_geom(*d, keep);
+    const thinkkv::ScoreGeom g = thinkkv::score_geom(*d);
+    const size_t need = g.ws_bytes > sg.ws_bytes ? g.ws_bytes : sg.ws_bytes;
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return THINK_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    thinkkv::SrPlan pl;
+    // the window rows are read through one 32-bit buffer range
+    const bool q_fits = (int64_t)d->batch * obs_window * d->n_q_heads * d->head_dim *
+                                thinkkv::elem_bytes(d->dtype) < ((int64_t)1 << 31);
+    if (q_fits && thinkkv::single_read_plan(*d, keep, sg, &pl))
+        return hip_status(thinkkv::launch_single_read(*d, sg, pl, k_cache, seq_lens,
+                                                      q_obs, obs_window, scores, keep, kept_idx,
+                                                      near_tie, k_thin, workspace, s));
+    st = hip_status(thinkkv::launch_score(*d, g, k_cache, seq_lens, q_obs, obs_window, scores,
+                                          workspace, keep, kept_idx, near_tie, s));
+    if (st != THINK_OK) return st;
+    return hip_status(thinkkv::launch_compact(*d, thinkkv::compact_geom(*d, keep), k_cache,
+                                              seq_lens, kept_idx, keep, k_thin, s));
+}
+
 namespace {
 
 // Validation shared by the decode entry points, in the documented order:

@@ -213,6 +213,32 @@ struct CompactGeom {
 };
 CompactGeom compact_geom(const think_dims& d, int keep);
 
+// Single-read score + select + compaction (one launch, K held in
+// registers between the phases).  Workspace: fp32 partials [<= 512 tiles][R],
+// then Q2 [B][Hq][D] fp64, then the tile flags [512], the selection flags
+// [B][Hkv] (64-bit) and an error word.
+constexpr int kSrMaxWorkgroups = 512;
+struct SingleReadGeom {
+    size_t part_bytes;
+    size_t q2_offset;
+    size_t bar_offset;
+    size_t ws_bytes;
+    bool shape_ok;     // the shape suits the kernel (the device decides the rest)
+};
+struct SrPlan {
+    int nv;            // 16-byte vectors per thread
+    int wps;           // workgroups per sequence
+    int rpw;           // token rows per workgroup
+    size_t lds;        // dynamic LDS bytes
+};
+SingleReadGeom single_read_geom(const think_dims& d, int keep);
+bool single_read_plan(const think_dims& d, int keep, const SingleReadGeom& g, SrPlan* plan);
+hipError_t launch_single_read(const think_dims& d, const SingleReadGeom& g, const SrPlan& plan,
+                              const void* k_cache, const int32_t* seq_lens,
+                              const void* q_obs, int W, float* scores, int keep,
+                              int32_t* kept_idx, int32_t* near_tie, void* k_thin,
+                              void* workspace, hipStream_t s);
+
 // ---------------------------------------------------------------------------
 // Launchers (return hipGetLastError() after enqueueing).
 // ---------------------------------------------------------------------------

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_header_declarations_are_all_exported(L):
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 21
     assert sorted(L.EXPORTS) == names
     so = ctypes.CDLL(L.LIB_PATH)
     for n in names:
@@ -42,7 +42,7 @@ def test_only_the_abi_is_exported(L):
 
 def test_version_and_keep_rounding(L):
     lib = L.lib
-    assert lib.think_abi_version() == 4
+    assert lib.think_abi_version() == 5
     assert [lib.think_keep_from_ratio(128, r) for r in (0.4, 0.6, 0.5)] == [77, 51, 64]
     assert lib.think_keep_from_ratio(16, 0.5) == 8
     assert lib.think_keep_from_ratio(128, 0.0) == 128
@@ -172,6 +172,38 @@ def test_append_decode_validation(L):
              None) == -6
     assert f(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 0.1, FAKE, None, big,
              None) == -6
+
+
+def test_score_select_compact_validation(L):
+    lib = L.lib
+    d = dims(L)
+    big = 1 << 30
+    f = lib.think_score_select_compact
+    # k_cache, seq_lens, q_obs, W, keep, scores, kept_idx, near_tie, k_thin, ws, bytes, stream
+    assert f(None, FAKE, FAKE, FAKE, 32, 8, FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == -1
+    for i in (0, 1, 2, 4, 6):                            # k_cache, seq_lens, q_obs, kept_idx, k_thin
+        args = [FAKE] * 7
+        args[i] = None
+        k, lens, qo, sc, idx, tie, kt = args
+        assert f(ctypes.byref(d), k, lens, qo, 32, 8, sc, idx, tie, kt, FAKE, big, None) == -1, i
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, 0, 8, FAKE, FAKE, FAKE, FAKE, FAKE, big,
+             None) == -2
+    for keep in (0, 129):
+        assert f(ctypes.byref(d), FAKE, FAKE, FAKE, 32, keep, FAKE, FAKE, FAKE, FAKE, FAKE, big,
+                 None) == -3
+    odd = ctypes.c_void_p(0x100008)
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, 32, 8, FAKE, FAKE, FAKE, odd, FAKE, big,
+             None) == -5
+    need = lib.think_score_compact_workspace_bytes(ctypes.byref(d), 8)
+    assert need >= lib.think_score_workspace_bytes(ctypes.byref(d))
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, 32, 8, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1,
+             None) == -6
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, 32, 8, FAKE, FAKE, FAKE, FAKE, None, big,
+             None) == -6
+    assert lib.think_score_compact_workspace_bytes(ctypes.byref(d), 0) == 0
+    assert lib.think_score_compact_single_read(None, 8) == -1
+    assert lib.think_score_compact_single_read(ctypes.byref(d), 0) == -3
+    assert lib.think_score_compact_single_read(ctypes.byref(d), 8) in (0, 1)
 
 
 def test_null_keep_window_workspace_and_alignment(L):

@@ -83,3 +83,53 @@ def test_append_then_decode(case, fused):
         print(f"[append] seed {seed} step {step}: lens {o_lens.tolist()}, "
               f"decode row err {err.max():.2e}", flush=True)
     assert (o_lens == np.minimum(lens + 3, S)).all()
+
+
+def test_random_fused_append_decode_shapes_match_the_oracle():
+    """Seeded random shapes through think_append_decode_attn, two steps each:
+    bf16 (matrix-core decode at head_dim 128, general decode otherwise) and
+    fp32, batches of 1-70 with empty, partial and full sequences, every kind
+    of keep.  Caches and lengths byte for byte against the oracle's append,
+    output rows within the decode bound of the oracle's decode over them."""
+    import query_driven_kv_amd as qdk
+    rng = np.random.default_rng(4242)
+    for case in range(32):
+        dtype = "f32" if case % 4 == 3 else "bf16"
+        D = 128 if (dtype == "bf16" and case % 3) else int(rng.choice([8, 64, 128, 256]))
+        B = int(rng.choice([1, 1, 2, 3, 8, 64, 70]))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 2, 4, 7]))
+        while Hkv * D * (2 if dtype == "bf16" else 4) > 32768:
+            Hkv //= 2
+        S = int(rng.integers(1, 2000)) if B <= 8 else int(rng.integers(1, 200))
+        keep = int(rng.integers(1, D + 1))
+        lens = rng.integers(0, S + 1, B).astype(np.int32)
+        lens[0] = S if case % 2 else 0
+        print(f"[fused case {case}] {dtype} B={B} Hkv={Hkv} G={G} D={D} S={S} keep={keep}",
+              flush=True)
+        sd = kvsynth.storage_dtype(dtype)
+
+        def draw(*shape):
+            x = rng.standard_normal(shape).astype(np.float32)
+            return kvsynth.to_bf16_bits(x) if dtype == "bf16" else x
+
+        thin, v = draw(B, S, Hkv, keep), draw(B, S, Hkv, D)
+        idx = np.sort(np.stack([np.stack([rng.choice(D, keep, replace=False)
+                                          for _ in range(Hkv)]) for _ in range(B)]),
+                      axis=-1).astype(np.int32)
+        thin_d, v_d, lens_d, idx_d = to_dev(thin), to_dev(v), to_dev(lens), to_dev(idx)
+        scale = np.float32(1.0 / np.sqrt(D))
+        o_thin, o_v, o_lens = thin, v, lens
+        for step in range(2):
+            q, k_new, v_new = draw(B, Hkv * G, D), draw(B, Hkv, D), draw(B, Hkv, D)
+            assert q.dtype == sd
+            out = qdk.think_append_decode_attn(to_dev(q), to_dev(k_new), to_dev(v_new), thin_d,
+                                               v_d, lens_d, idx_d, scale)
+            torch.cuda.synchronize()
+            o_thin, o_v, o_lens = oracle.append(k_new, v_new, o_lens, idx, o_thin, o_v)
+            np.testing.assert_array_equal(to_host(lens_d), o_lens)
+            np.testing.assert_array_equal(to_host(thin_d).view(np.uint8), o_thin.view(np.uint8))
+            np.testing.assert_array_equal(to_host(v_d).view(np.uint8), o_v.view(np.uint8))
+            ref = oracle.decode(q, o_thin, o_v, o_lens, idx, scale)
+            err = row_rel_err(out, ref).max()
+            assert err <= tol_for(dtype), (case, step, err)
