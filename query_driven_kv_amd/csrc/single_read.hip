@@ -29,7 +29,9 @@
 //            compaction does).
 //
 // A flag is a 64-bit word in the caller's workspace set to a tag that is new
-// for every launch, so a workspace with any previous contents works.  Every
+// for every launch (a generation word in the workspace that every launch
+// advances, so graph replays differ too, with the call's own counter below
+// it), so a workspace with any previous contents works.  Every
 // flag has one writer, which stores it; waiters read it with an atomic add of
 // zero (no counter that every workgroup updates, which serialised the
 // arrivals and cost about 1 ms per call when tried).  The
@@ -103,7 +105,8 @@ struct SrParams {
     unsigned long long* tile_done;   // [nwg] flags
     unsigned long long* selected;    // [B][Hkv][ceil(D/16)] tag << 16 | 16 mask bits
     unsigned* err;                   // set if a wait ran out
-    unsigned long long tag;
+    unsigned long long* gen;         // launch generation, advanced by every launch
+    unsigned long long tag;          // per call, low 24 bits nonzero (frozen in a captured graph)
     int s_cap, nvec, rpw, wps, nb, W, nqv, Hq, Hkv, D, keep;
 };
 
@@ -122,6 +125,14 @@ __global__ __launch_bounds__(kSrThreads) void k_score_compact_resident(SrParams 
     const int len = clamp_len(p.seq_lens, b, p.s_cap);
     const int nt = max(0, min(p.rpw, len - t0));  // valid rows of this tile
     if (w == 0 && tid == 0) *p.err = 0u;          // set only if a wait runs out
+    // the flags' 48-bit tag: the workspace's launch generation (which
+    // workgroup 0 advances once every workgroup has read it) above the call's
+    // 24-bit value.  Launches on one workspace differ in the generation, so
+    // replays of a captured launch, whose arguments are frozen, tag afresh
+    // too; the call's value guards against a workspace of unrelated bytes.
+    const unsigned long long gen =
+            __hip_atomic_load(p.gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long tag = ((gen & 0xffffffull) << 24) | (p.tag & 0xffffffull);
 
     // ---- phase 1: the tile into registers (vector tid + k*512 of the tile;
     // nvec divides 512, so every vector of a thread is in column tid % nvec)
@@ -213,11 +224,14 @@ __global__ __launch_bounds__(kSrThreads) void k_score_compact_resident(SrParams 
         }
     }
 
-    signal_flag(p.tile_done + w, p.tag);
+    signal_flag(p.tile_done + w, tag);
 
     // ---- phase 2: scores and selection, one workgroup per (b, kv)
     if (w < p.nb * p.Hkv) {
-        wait_flags(p.tile_done, nwg, p.tag, p.err);
+        wait_flags(p.tile_done, nwg, tag, p.err);
+        // every workgroup has stored its flag, so every one has read gen
+        if (w == 0 && tid == 0)
+            __hip_atomic_store(p.gen, gen + 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int bb = w / p.Hkv, kv = w - bb * p.Hkv;
         const int D = p.D, G = p.Hq / p.Hkv, Q = D / 4, SG = kSrThreads / Q;
         const int lenb = clamp_len(p.seq_lens, bb, p.s_cap);
@@ -282,7 +296,7 @@ __global__ __launch_bounds__(kSrThreads) void k_score_compact_resident(SrParams 
         const int nw = (D + 15) / 16;
         if (tid < nw)
             __hip_atomic_store(p.selected + row * nw + tid,
-                               (p.tag << 16) | ((s_mask[tid / 2] >> (16 * (tid % 2))) & 0xffffu),
+                               (tag << 16) | ((s_mask[tid / 2] >> (16 * (tid % 2))) & 0xffffu),
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
@@ -300,7 +314,7 @@ __global__ __launch_bounds__(kSrThreads) void k_score_compact_resident(SrParams 
             for (uint32_t spin = 0;; ++spin) {
                 x = __hip_atomic_fetch_add(words + i, 0ull, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
-                if ((x >> 16) == p.tag) break;
+                if ((x >> 16) == tag) break;
                 if (spin == kSrSpinLimit) {
                     __hip_atomic_store(p.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     break;
@@ -437,12 +451,15 @@ const void* sr_kernel_for(int dtype, int nv) {
     return nullptr;
 }
 
-// a tag not used by any earlier launch of this process (40 bits, never 0)
+// the call's share of the tag: a process-wide counter seeded from the clock,
+// 24 bits, never 0
 unsigned long long next_tag() {
     static std::atomic<unsigned long long> counter{
             (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count()};
-    const unsigned long long t = counter.fetch_add(1) & ((1ull << 40) - 1);
-    return t ? t : 1;
+    for (;;) {
+        const unsigned long long t = counter.fetch_add(1) & 0xffffffull;
+        if (t) return t;
+    }
 }
 
 }  // namespace
@@ -456,7 +473,8 @@ SingleReadGeom single_read_geom(const think_dims& d, int keep) {
     g.q2_offset = g.part_bytes;
     g.bar_offset = g.q2_offset +
                    ((size_t)d.batch * d.n_q_heads * d.head_dim * sizeof(double) + 15) / 16 * 16;
-    // tile flags [kSrMaxWorkgroups], mask words [B][Hkv][ceil(D/32)], the error word
+    // tile flags [kSrMaxWorkgroups], mask words [B][Hkv][ceil(D/16)], the error
+    // word and the launch generation
     g.ws_bytes = g.bar_offset +
                  ((size_t)kSrMaxWorkgroups +
                   (size_t)d.batch * d.n_kv_heads * ((d.head_dim + 15) / 16)) * 8 + 16;
@@ -520,6 +538,7 @@ hipError_t launch_single_read(const think_dims& d, const SingleReadGeom& g, cons
     p.selected = p.tile_done + kSrMaxWorkgroups;
     p.err = reinterpret_cast<unsigned*>(p.selected + (size_t)d.batch * d.n_kv_heads *
                                                           ((d.head_dim + 15) / 16));
+    p.gen = reinterpret_cast<unsigned long long*>(p.err) + 1;
     p.tag = next_tag();
     p.s_cap = d.seq_capacity;
     p.nvec = d.n_kv_heads * d.head_dim * elem_bytes(d.dtype) / 16;

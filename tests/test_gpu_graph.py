@@ -66,3 +66,59 @@ def test_pruning_and_decode_step_replays_in_a_graph():
             x = torch.randn(1 << 20, device="cuda").sum()   # unrelated eager work
             torch.cuda.synchronize()
             assert torch.isfinite(x)
+
+
+def test_single_read_pruning_replays_in_a_graph():
+    """The single-read pruning launch tags its flags with the call's value plus
+    a generation word in the workspace that every launch advances, so replays
+    of a captured call (frozen arguments) do not see the previous replay's
+    flags.  New keys are copied into the static buffer before every replay,
+    and eager calls on the same workspace run in between; every replay must
+    give the eager call's bits."""
+    import query_driven_kv_amd as qdk
+    B, Hq, Hkv, D, S, keep = 1, 8, 2, 128, 4096, 51
+    cfg = kvsynth.custom("graph-sr", batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D,
+                         seq_capacity=S, obs_window=8, keep=keep, dtype="bf16", lowrank=8,
+                         cfg_id=94)
+    dims = qdk.make_dims(B, Hq, Hkv, D, S, torch.bfloat16)
+    assert qdk.think_score_compact_single_read(dims, keep) == 1
+    layers = [kvsynth.make_layer(cfg, layer=l) for l in range(3)]
+    keys = [to_dev(L["k_cache"]) for L in layers]
+    k = torch.empty_like(keys[0])
+    lens = to_dev(np.array([4000], np.int32))
+    qo = to_dev(layers[0]["q_obs"])
+    scores = torch.empty(B, Hkv, D, dtype=torch.float32, device="cuda")
+    idx = torch.empty(B, Hkv, keep, dtype=torch.int32, device="cuda")
+    tie = torch.empty(B, Hkv, dtype=torch.int32, device="cuda")
+    thin = torch.zeros(B, S, Hkv, keep, dtype=torch.bfloat16, device="cuda")
+    ws = torch.randint(0, 256, (qdk.think_score_compact_workspace_bytes(dims, keep),),
+                       dtype=torch.uint8).cuda()
+
+    def call(kbuf, s_out, i_out, t_out, th_out):
+        qdk.think_score_select_compact(kbuf, lens, qo, keep, scores=s_out, kept_idx=i_out,
+                                       near_tie=t_out, k_thin=th_out, workspace=ws)
+
+    k.copy_(keys[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(k, scores, idx, tie, thin)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(k, scores, idx, tie, thin)
+    torch.cuda.synchronize()
+
+    for rep in range(6):
+        k.copy_(keys[rep % 3])
+        g.replay()
+        got = [t.clone() for t in (scores, idx, tie, thin)]
+        torch.cuda.synchronize()
+        ref = [torch.empty_like(t) for t in (scores, idx, tie, thin)]
+        ref[3].zero_()
+        call(keys[rep % 3], *ref)                    # eager, same workspace
+        torch.cuda.synchronize()
+        for a, b in zip(got, ref):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), rep
+        print(f"[graph-sr] replay {rep} on layer {rep % 3}: equal to the eager call", flush=True)
