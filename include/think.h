@@ -160,9 +160,11 @@ THINK_API int think_compact_k(const think_dims *d, const void *k_cache, const in
  * differ in the last fp32 place: the token sums are split differently) and,
  * for the same kept channels, the same k_thin bytes.
  *   workspace   >= think_score_compact_workspace_bytes(d, keep) bytes, 16-byte
- *               aligned, any previous contents (the single-read launch keeps
- *               a barrier counter there, tagged per launch; calls that share a
- *               workspace must not overlap in time)
+ *               aligned, any previous contents.  The single-read launch keeps
+ *               its flags there, tagged with a generation word that every
+ *               launch advances, so the call may be captured in a graph and
+ *               replayed; calls that share a workspace must not overlap in
+ *               time.
  */
 THINK_API int think_score_select_compact(const think_dims *d, const void *k_cache,
                                          const int32_t *seq_lens, const void *q_obs,
