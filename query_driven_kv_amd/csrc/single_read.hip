@@ -498,7 +498,8 @@ bool single_read_plan(const think_dims& d, int keep, const SingleReadGeom& g, Sr
     const int nvec = d.n_kv_heads * d.head_dim * elem_bytes(d.dtype) / 16;
     int slots = ncu < kSrMaxWorkgroups ? ncu : kSrMaxWorkgroups;
     const int wps = slots / d.batch;
-    if (wps < 1) return false;
+    // every (b, kv) row is selected by workgroup b*Hkv + kv of the grid
+    if (wps < 1 || d.n_kv_heads > wps) return false;
     const int rpw = (d.seq_capacity + wps - 1) / wps;
     const int64_t need = (int64_t)rpw * nvec;    // vectors per tile
     int nv = 0;

@@ -117,7 +117,7 @@ def _fits(c):
         return False
     ncu = min(torch.cuda.get_device_properties(0).multi_processor_count, 512)
     wps = ncu // c["batch"]
-    if wps < 1:
+    if wps < 1 or c["n_kv_heads"] > wps:          # one selecting workgroup per (b, kv)
         return False
     rpw = -(-c["seq_capacity"] // wps)
     return rpw * nvec <= 32 * 512
@@ -141,6 +141,12 @@ EXTRA = [
     # a key cache just past what fits (two passes)
     dict(seed=42, lens=[33000], batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128,
          seq_capacity=33000, keep=64, dtype="bf16", lowrank=8),
+    # 32 sequences of 8 kv heads: exactly one selecting workgroup per (b, kv)
+    # row fits (8 workgroups per sequence); 40 sequences do not (two passes)
+    dict(seed=44, lens=[(i * 131) % 600 + 1 for i in range(32)], batch=32, n_q_heads=32,
+         n_kv_heads=8, head_dim=128, seq_capacity=600, keep=64, dtype="bf16", lowrank=8),
+    dict(seed=45, lens=[(i * 97) % 300 + 1 for i in range(40)], batch=40, n_q_heads=32,
+         n_kv_heads=8, head_dim=128, seq_capacity=300, keep=64, dtype="bf16", lowrank=8),
     # more sequences than compute units (two passes)
     dict(seed=43, lens=[(i * 7) % 50 + 1 for i in range(300)], batch=300, n_q_heads=2,
          n_kv_heads=1, head_dim=128, seq_capacity=50, keep=64, dtype="bf16"),
