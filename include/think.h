@@ -19,8 +19,12 @@
  *  - Arguments are validated on the host before anything is enqueued.  On an
  *    error nothing is enqueued and a negative think_status is returned.
  *  - Outputs must not alias inputs.  Calls on different streams are
- *    independent and may run concurrently; calls that share a workspace must
- *    be ordered by the caller.
+ *    independent and may run concurrently, with one exception: the
+ *    single-read launch of think_score_select_compact, whose workgroups wait
+ *    for one another, must not run concurrently with another such launch
+ *    (two could each hold half the compute units while waiting for the
+ *    other half).  Calls that share a workspace must be ordered by the
+ *    caller.
  *  - `seq_lens` is device memory: int32 [B], each 1 <= len_b <= S_cap (the
  *    host cannot check device values; kernels clamp them to [0, S_cap], and a
  *    length of 0 yields zero scores / zero attention output for that batch).
@@ -154,8 +158,11 @@ THINK_API int think_compact_k(const think_dims *d, const void *k_cache, const in
  * think_score_compact_single_read), one launch of one workgroup per compute
  * unit reads K once, holds it on chip while the channels are selected and
  * writes k_thin from there; otherwise the two-pass kernels run.  The
- * workgroups of that launch wait for one another (bounded waits), so it
- * should not share the device with a kernel that never finishes.
+ * workgroups of that launch wait for one another, so it needs every compute
+ * unit to become free in time: it must not run concurrently with another
+ * single-read launch or share the device with a kernel that never finishes.
+ * Its waits are bounded (about 4 s), so a violation ends with wrong outputs
+ * rather than a hang.
  * Both paths give the same kept channels up to the near-tie flag (scores may
  * differ in the last fp32 place: the token sums are split differently) and,
  * for the same kept channels, the same k_thin bytes.
