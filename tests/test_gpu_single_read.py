@@ -159,3 +159,25 @@ def test_extra_shapes(case):
     seed, lens = c.pop("seed"), c.pop("lens")
     cfg, L, _ = _custom(seed, lens, **c)
     check_single_read(cfg, L, cfg.keep, f"extra{seed}", _fits(case))
+
+
+def test_random_shapes():
+    """Seeded random shapes through the one-call pruning: bf16 and fp32, head
+    dims 8-256, batches of 1-40 with ragged lengths, every kind of keep and
+    window; each states its route and passes the checks above."""
+    rng = np.random.default_rng(909)
+    for case in range(16):
+        dtype = "f32" if case % 4 == 3 else "bf16"
+        D = int(rng.choice([8, 32, 64, 128, 128, 256]))
+        B = int(rng.choice([1, 1, 2, 5, 16, 40]))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 2, 4]))
+        while Hkv * D * (2 if dtype == "bf16" else 4) > 32768:
+            Hkv //= 2
+        S = int(rng.integers(1, 3000)) if B <= 5 else int(rng.integers(1, 400))
+        keep = int(rng.integers(1, D + 1))
+        lens = [int(x) for x in rng.integers(1, S + 1, B)]
+        c = dict(batch=B, n_q_heads=Hkv * G, n_kv_heads=Hkv, head_dim=D, seq_capacity=S,
+                 keep=keep, dtype=dtype, obs_window=int(rng.integers(1, 65)))
+        cfg, L, _ = _custom(200 + case, lens, **c)
+        check_single_read(cfg, L, keep, f"random{case}", _fits(c))
