@@ -286,7 +286,10 @@ def test_split_phase_decode_is_bitwise_the_single_call():
     qdk = _qdk()
     for seed, lens, Hq, Hkv, D, keep, dtype in [(40, [3000, 17], 8, 2, 128, 64, "bf16"),
                                                 (41, [900], 6, 3, 64, 20, "f32"),
-                                                (42, [2048, 2047], 32, 8, 128, 77, "bf16")]:
+                                                (42, [2048, 2047], 32, 8, 128, 77, "bf16"),
+                                                (43, [30000], 32, 8, 128, 51, "bf16"),
+                                                (44, [(i * 97) % 2000 + 1 for i in range(70)],
+                                                 2, 1, 128, 96, "bf16")]:
         cfg, L, q = _custom(seed, lens, batch=len(lens), n_q_heads=Hq, n_kv_heads=Hkv,
                             head_dim=D, seq_capacity=max(lens), keep=keep, dtype=dtype,
                             obs_window=4)
