@@ -31,18 +31,20 @@
 // A flag is a 64-bit word in the caller's workspace set to a tag that is new
 // for every launch (a generation word in the workspace that every launch
 // advances, so graph replays differ too, with the call's own counter below
-// it), so a workspace with any previous contents works.  Every
-// flag has one writer, which stores it; waiters read it with an atomic add of
-// zero (no counter that every workgroup updates, which serialised the
-// arrivals and cost about 1 ms per call when tried).  The
-// grid is at most one workgroup per compute unit and the occupancy query
-// confirms that one fits, so every workgroup is resident at once, or becomes
-// resident as soon as work launched before it on other streams drains: a
-// waiting workgroup never keeps a producer from being scheduled.  Every wait
-// is bounded all the same: should one ever run out, the kernel sets an error
-// word and finishes.  (A cooperative launch, which the runtime refuses
-// unless all workgroups fit at once, cost about 17 us more per call here.)
-// No float atomics: results are bitwise reproducible.
+// it), so a workspace with any previous contents works.  Every flag has one
+// writer, which stores it after a release fence; waiters read it with an
+// atomic add of zero, which the memory system performs on the current value
+// (a plain load kept returning a copy cached in this chiplet's L2), then take
+// one acquire fence.  (One arrival counter updated by every workgroup
+// serialised the arrivals: about 1 ms per call when tried.)  The grid is at
+// most one workgroup per compute unit and the occupancy query confirms that
+// one fits, so every workgroup is resident at once, or becomes resident as
+// the workgroups of other kernels finish; two launches of this kind running
+// at once could each hold part of the device, which the interface forbids.
+// Every wait is bounded all the same: should one run out, the kernel sets an
+// error word and finishes, so nothing hangs.  (A cooperative launch, which
+// the runtime refuses unless all workgroups fit at once, cost about 17 us
+// more per call here.)  No float atomics: results are bitwise reproducible.
 #include <atomic>
 #include <chrono>
 
