@@ -10,7 +10,7 @@
 // workgroup per compute unit reads it once:
 //
 //   phase 1  every workgroup (one per CU) loads its tile of token rows of one
-//            sequence into registers (16-byte vectors, all loads in flight at
+//            sequence (each XCD a contiguous run of tiles) into registers (16-byte vectors, all loads in flight at
 //            once), sums the per-channel squares of the tile (fp32 runs of
 //            <= 16 tokens folded into fp64, the rows of a column reduced in
 //            LDS in a fixed order) and writes one fp32 partial per channel;
@@ -121,7 +121,14 @@ __global__ __launch_bounds__(kSrThreads) void k_score_compact_resident(SrParams 
     extern __shared__ uint4 lds[];
     const int w = blockIdx.x, nwg = gridDim.x;
     const int tid = threadIdx.x;
-    const int b = w / p.wps, part = w - b * p.wps;
+    // tile number: consecutive workgroups are dealt round-robin over the 8
+    // XCDs, so tw gives each XCD one contiguous run of tiles; tiles
+    // interleaved between the XCDs every 256 KiB stream K a third slower.
+    // The selection roles of phase 2 (and the window-query units) keep the
+    // hardware order w, which spreads them over every XCD.
+    const int xcd = w % 8;
+    const int tw = xcd * (nwg / 8) + min(xcd, nwg % 8) + w / 8;
+    const int b = tw / p.wps, part = tw - b * p.wps;
     const int nvec = p.nvec, R = nvec * EPV;     // channels per token row (Hkv*D)
     const int t0 = part * p.rpw;
     const int len = clamp_len(p.seq_lens, b, p.s_cap);
@@ -189,7 +196,7 @@ __global__ __launch_bounds__(kSrThreads) void k_score_compact_resident(SrParams 
     for (int o = tid; o < R; o += kSrThreads) {
         double s = 0.0;
         for (int r = 0; r < nsub; ++r) s += red[r * R + o];
-        p.partials[(size_t)w * R + o] = (float)s;
+        p.partials[(size_t)tw * R + o] = (float)s;
     }
 
     // window-query sums of squares of this workgroup's units: each thread
@@ -226,7 +233,7 @@ __global__ __launch_bounds__(kSrThreads) void k_score_compact_resident(SrParams 
         }
     }
 
-    signal_flag(p.tile_done + w, tag);
+    signal_flag(p.tile_done + tw, tag);
 
     // ---- phase 2: scores and selection, one workgroup per (b, kv)
     if (w < p.nb * p.Hkv) {
