@@ -316,6 +316,10 @@ __global__ __launch_bounds__(kSrThreads) void k_score_compact_resident(SrParams 
     uint16_t* srcmap = reinterpret_cast<uint16_t*>(lds + SK * kSrThreads);
     uint32_t* kmask = reinterpret_cast<uint32_t*>(srcmap + (Ro + 7) / 8 * 8);   // [Hkv][nw]
     const int nw = (p.D + 15) / 16;
+    // phase 2's LDS is free once its mask chunks are published (with 4 vectors
+    // per thread the arrays below start at 32 KiB and can reach them)
+    __syncthreads();
+    for (int o = tid; o < Ro; o += kSrThreads) srcmap[o] = 0;  // only a torn mask leaves gaps
     {
         unsigned long long* words = p.selected + (size_t)b * p.Hkv * nw;
         for (int i = tid; i < p.Hkv * nw; i += kSrThreads) {
@@ -334,25 +338,17 @@ __global__ __launch_bounds__(kSrThreads) void k_score_compact_resident(SrParams 
         }
     }
     __syncthreads();
-    // srcmap[kv*keep + j] = kv*D + (the j-th kept channel of head kv): every
-    // kept channel finds its slot j by counting the kept channels below it
-    // (whole 16-bit chunks first, from a per-chunk prefix count)
-    uint32_t* kpre = kmask + p.Hkv * nw;                     // [Hkv][nw]
+    // srcmap[kv*keep + j] = kv*D + (the j-th kept channel of head kv): one
+    // thread per 16-bit chunk counts the kept channels of the chunks below it,
+    // then hands out the next slots to its own kept channels in ascending order
     for (int i = tid; i < p.Hkv * nw; i += kSrThreads) {
         const int kv = i / nw, wi = i - kv * nw;
-        int n = 0;
-        for (int x = 0; x < wi; ++x) n += __popc(kmask[kv * nw + x]);
-        kpre[i] = (uint32_t)n;
-    }
-    for (int o = tid; o < Ro; o += kSrThreads) srcmap[o] = 0;  // only a torn mask leaves gaps
-    __syncthreads();
-    for (int ch = tid; ch < p.Hkv * p.D; ch += kSrThreads) {
-        const int kv = ch / p.D, c = ch - kv * p.D;
-        const uint32_t m = kmask[kv * nw + c / 16];
-        const int bit = c % 16;
-        if ((m >> bit) & 1u) {
-            const int j = (int)kpre[kv * nw + c / 16] + __popc(m & ((1u << bit) - 1u));
-            if (j < keep) srcmap[kv * keep + j] = (uint16_t)ch;
+        int j = 0;
+        for (int x = 0; x < wi; ++x) j += __popc(kmask[kv * nw + x]);
+        for (uint32_t m = kmask[i]; m != 0u; m &= m - 1u) {
+            const int c = wi * 16 + __builtin_ctz(m);
+            if (j < keep && c < p.D) srcmap[kv * keep + j] = (uint16_t)(kv * p.D + c);
+            ++j;
         }
     }
     T* k_thin = static_cast<T*>(p.k_thin);
