@@ -54,6 +54,15 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=0,
                     help="override the workload's decode steps (profiling runs only; "
                          "reported in config)")
+    ap.add_argument("--also", default="mistral-7b-gqa-32k",
+                    help="comma-separated workloads also measured in the same run, reported "
+                         "under 'also' (empty: none)")
+    ap.add_argument("--also-steps", type=int, default=200,
+                    help="timed steps of each workload under --also")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the append, append+decode and prefill figures")
+    ap.add_argument("--parity", action="store_true",
+                    help="with --no-cpu-baseline: still check layer 0 against the oracle")
     return ap.parse_args()
 
 
@@ -397,43 +406,267 @@ def committed_traffic(workload):
     return int(rec["hbm_bytes_per_launch"]), rec.get("command", "")
 
 
-def cpu_baseline(wl, budget_s):
-    """The oracle, untuned, on a bounded sample of the same workload: full
-    score+select+compact of layer 0, then decode steps of layer 0 until the
-    time budget is spent.  Same algorithmic byte accounting as the GPU."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            return next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        return ""
+
+
+def oracle_sample(wl, budget_s, threads):
+    """The oracle, untuned, at `threads` OpenMP threads on a bounded sample of
+    the same workload: full score+select+compact of layer 0, then decode steps
+    of layer 0 until the time budget is spent.  Same algorithmic byte
+    accounting as the GPU.  Returns the figures and the oracle's outputs
+    (scores, kept channels, near-tie flags, thin keys, step-0 decode rows)."""
     import oracle
     cfg, L = wl.cfg, wl.host0
     bm = wl.bytes_model()
-    threads = oracle.num_threads()
+    oracle.set_threads(threads)
+    used = oracle.num_threads()
     t0 = time.perf_counter()
     s = oracle.score(L["k_cache"], L["seq_lens"], L["q_obs"])
-    idx, _ = oracle.select(s, cfg.keep)
+    idx, tie = oracle.select(s, cfg.keep)
     thin = oracle.compact(L["k_cache"], L["seq_lens"], idx)
     t_sc = time.perf_counter() - t0
     scale = np.float32(1.0 / np.sqrt(cfg.head_dim))
-    steps, t_dec = 0, 0.0
+    steps, t_dec, out0 = 0, 0.0, None
     while steps < cfg.decode_steps and (t_sc + t_dec < budget_s or steps == 0):
         q = kvsynth.decode_q(cfg, 0, steps, L["channel_scale"])
         t1 = time.perf_counter()
-        oracle.decode(q, thin, L["v_cache"], L["seq_lens"], idx, scale)
+        o = oracle.decode(q, thin, L["v_cache"], L["seq_lens"], idx, scale)
         t_dec += time.perf_counter() - t1
+        if steps == 0:
+            out0 = o
         steps += 1
     total_bytes = bm["sc_layer"] + steps * bm["dec_call"]
     total_s = t_sc + t_dec
-    model = ""
-    try:
-        with open("/proc/cpuinfo") as f:
-            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
-    except OSError:
-        pass
-    return {"value": round(total_bytes / total_s / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "cpu": model,
-            "sample": (f"layer 0 of {cfg.name}: score+select+compact once ({t_sc:.2f}s) and "
-                       f"{steps} decode steps ({t_dec:.2f}s); fp64 C oracle, OpenMP over "
-                       f"(batch, head) pairs, {threads} threads"),
-            "seconds": round(total_s, 2),
-            "score_compact_GBps": round(bm["sc_layer"] / t_sc / 1e9, 4),
-            "decode_GBps": round(steps * bm["dec_call"] / max(t_dec, 1e-9) / 1e9, 4)}
+    fig = {"value": round(total_bytes / total_s / 1e9, 4), "unit": "GB/s", "cores": used,
+           "seconds": round(total_s, 2),
+           "sample": (f"layer 0 of {cfg.name}: score+select+compact once ({t_sc:.2f}s) and "
+                      f"{steps} decode steps ({t_dec:.2f}s); fp64 C oracle, OpenMP over "
+                      f"(batch, head) pairs, {used} threads"),
+           "score_compact_GBps": round(bm["sc_layer"] / t_sc / 1e9, 4),
+           "decode_GBps": round(steps * bm["dec_call"] / max(t_dec, 1e-9) / 1e9, 4)}
+    return fig, dict(scores=s, idx=idx, tie=tie, thin=thin, out0=out0)
+
+
+def cpu_baseline(wl, budget_s):
+    """The oracle at all host threads (the reported figure) and at one thread,
+    each on its own bounded sample; returns the record and the oracle outputs
+    of the all-threads run."""
+    nthreads = len(os.sched_getaffinity(0))
+    fig, ref = oracle_sample(wl, budget_s, nthreads)
+    one, _ = oracle_sample(wl, max(budget_s * 0.6, 1.0), 1)
+    rec = {"value": fig["value"], "unit": "GB/s", "cores": fig["cores"], "kind": "oracle",
+           "cpu": _cpu_model(), "sample": fig["sample"], "seconds": fig["seconds"],
+           "score_compact_GBps": fig["score_compact_GBps"], "decode_GBps": fig["decode_GBps"],
+           "single_thread": {k: one[k] for k in ("value", "cores", "seconds", "sample",
+                                                  "score_compact_GBps", "decode_GBps")}}
+    return rec, ref
+
+
+def gpu_layer0(wl, torch):
+    """Layer 0 of the workload through the GPU path once more (copy 0's
+    inputs): scores, kept channels, near-tie flags, thin keys and the step-0
+    decode rows, on the host."""
+    from query_driven_kv_amd import _lib
+    lib, P = _lib.lib, ctypes.c_void_p
+    e = wl.layers[0]
+
+    def to_host(t):
+        t = t.detach().cpu().contiguous()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view(np.uint16)
+        return t.numpy()
+
+    d, keep = ctypes.byref(wl.dims), wl.cfg.keep
+    sp = P(torch.cuda.current_stream().cuda_stream)
+    _lib.check("think_score_select_compact", lib.think_score_select_compact(
+        d, P(e["k"].data_ptr()), P(e["lens"].data_ptr()), P(e["qo"].data_ptr()),
+        wl.cfg.obs_window, keep, P(e["scores"].data_ptr()), P(e["idx"].data_ptr()),
+        P(e["tie"].data_ptr()), P(e["thin"].data_ptr()), P(wl.ws_s.data_ptr()), wl.ws_s.numel(),
+        sp))
+    st = lib.think_score_compact_status(d, wl.cfg.obs_window, keep, P(wl.ws_s.data_ptr()),
+                                        wl.ws_s.numel(), sp)
+    out = torch.empty_like(wl.out)
+    _lib.check("think_decode_attn", lib.think_decode_attn(
+        d, P(e["q"].data_ptr()), P(e["thin"].data_ptr()), P(e["v"].data_ptr()),
+        P(e["lens"].data_ptr()), P(e["idx"].data_ptr()), keep, wl.scale, P(out.data_ptr()),
+        P(wl.ws_d.data_ptr()), wl.ws_d.numel(), sp))
+    torch.cuda.synchronize()
+    return dict(scores=to_host(e["scores"]), idx=to_host(e["idx"]), tie=to_host(e["tie"]),
+                thin=to_host(e["thin"]), out0=to_host(out), status=st)
+
+
+def parity(wl, g, ref):
+    """The GPU's layer-0 outputs against the oracle's on the same bytes: kept
+    channels bit-exact outside reported near ties, thin keys bit-exact, decode
+    rows within the dtype's bound, scores within 5e-6 relative."""
+    cfg = wl.cfg
+    lens = wl.lens_host
+    rel_s = float((np.abs(g["scores"].astype(np.float64) - ref["scores"]) /
+                   np.maximum(ref["scores"], 1e-30)).max())
+    rows_diff = (g["idx"] != ref["idx"]).any(axis=-1)
+    outside = int((rows_diff & (ref["tie"] == 0)).sum())
+    thin_ref, out_ref = ref["thin"], ref["out0"]
+    if rows_diff.any():
+        # a near tie went the other way: the thin keys and the decode are
+        # checked on the GPU's own channel choice
+        import oracle
+        L = wl.host0
+        thin_ref = oracle.compact(L["k_cache"], lens, g["idx"])
+        q = kvsynth.decode_q(cfg, 0, 0, L["channel_scale"])
+        out_ref = oracle.decode(q, thin_ref, L["v_cache"], lens, g["idx"],
+                                np.float32(1.0 / np.sqrt(cfg.head_dim)))
+    thin_ok = all(np.array_equal(g["thin"][b, :n].view(np.uint8), thin_ref[b, :n].view(np.uint8))
+                  for b, n in enumerate(lens))
+    of = kvsynth.as_float(g["out0"]).astype(np.float64)
+    den = np.maximum(np.abs(out_ref).max(axis=-1), 1e-300)
+    row_err = float((np.abs(of - out_ref).max(axis=-1) / den).max())
+    tol = 1e-5 if cfg.dtype == "f32" else 2e-2
+    rec = {"workload": cfg.name, "layer": 0, "decode_step": 0,
+           "scores_max_rel_err": float(f"{rel_s:.3e}"), "scores_tol": 5e-6,
+           "idx_bit_exact": bool(not rows_diff.any()),
+           "idx_rows_differing_outside_near_ties": outside,
+           "near_ties": int(ref["tie"].sum()),
+           "k_thin_bit_exact": bool(thin_ok),
+           "decode_row_err": float(f"{row_err:.3e}"), "decode_tol": tol,
+           "single_read_status": int(g["status"])}
+    rec["pass"] = bool(rel_s <= 5e-6 and outside == 0 and thin_ok and row_err <= tol
+                       and g["status"] == 0)
+    return rec
+
+
+def measure(cfg, args, torch, qdk, dev, steps, warmup, extras):
+    """Time `steps` whole steps of workload `cfg` (after `warmup`), then the
+    chunk-pass launches alone; with `extras`, the append, append+decode and
+    prefill figures too.  Returns (workload, record)."""
+    wl = Workload(cfg, torch, qdk, dev)
+    wl.prepare_decode()
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    bm = wl.bytes_model()
+    n_dec = cfg.decode_steps * cfg.layers
+
+    for _ in range(max(warmup, 1 if wl.ncopies > 1 else 0)):
+        for _ in range(wl.ncopies):              # every copy's thin cache is filled
+            wl.score_compact(sp)
+        wl.decode(sp)
+    torch.cuda.synchronize()
+    log(f"{cfg.name}: warmup done")
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        a, b, c = ev[k]
+        a.record(stream)
+        wl.score_compact(sp)
+        b.record(stream)
+        wl.decode(sp)
+        c.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sc_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    dec_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    log(f"{cfg.name}: timed {steps} steps: {wall:.3f}s wall, score+compact {sc_ms:.3f} ms, "
+        f"decode {dec_ms:.3f} ms per step")
+
+    ms_per_step = wall / steps * 1e3
+    sc_moved = bm["sc_min_layer"] if wl.single_read else bm["sc_layer"]
+    step_bytes = cfg.layers * sc_moved + n_dec * bm["dec_call"]
+    step_bytes_eff = cfg.layers * bm["sc_layer"] + n_dec * bm["dec_call"]
+    value = step_bytes / (ms_per_step / 1e3) / 1e9
+    tok = bm["tokens"]
+    kv_tok_s = (tok * cfg.layers * (1 + cfg.decode_steps)) / (ms_per_step / 1e3)
+    sc_gbs = cfg.layers * sc_moved / (sc_ms / 1e3) / 1e9
+    sc_eff = cfg.layers * bm["sc_layer"] / (sc_ms / 1e3) / 1e9
+    dec_gbs = n_dec * bm["dec_call"] / (dec_ms / 1e3) / 1e9
+    dec_call_us = dec_ms * 1e3 / n_dec
+    near = int(sum(int(e["tie"].sum().item()) for e in wl.layers))
+    # the dominant kernel's own launch duration, live, with HIP events (a
+    # separate pass after the timed region, so the events do not perturb it)
+    if args.no_kernel_timing:
+        part_us, n_part, part_pct = float("nan"), 0, None
+    else:
+        part_us, n_part, part_pct = wl.decode_kernel_times(sp, torch)
+        log(f"{cfg.name}: chunk-pass kernel: {part_us:.2f} us mean over {n_part} launches")
+    achieved = bm["dec_call"] / (part_us * 1e-6) / 1e9 if n_part else None
+    rec = {
+        "ms_per_step": round(ms_per_step, 4),
+        "GBps": round(value, 2),
+        "pct_of_peak": round(100 * value / PEAK_GBS, 2),
+        "GBps_effective": round(step_bytes_eff / (ms_per_step / 1e3) / 1e9, 2),
+        "bytes_per_step": step_bytes,
+        "kv_tokens_per_s": float(f"{kv_tok_s:.4g}"),
+        "paths": {
+            "score_compact": {"ms_per_step": round(sc_ms, 4),
+                              "us_per_layer": round(sc_ms * 1e3 / cfg.layers, 2),
+                              "GBps": round(sc_gbs, 1),
+                              "pct_of_peak": round(100 * sc_gbs / PEAK_GBS, 2),
+                              "bytes_moved_per_layer": sc_moved,
+                              "GBps_effective": round(sc_eff, 1),
+                              "pct_of_peak_effective": round(100 * sc_eff / PEAK_GBS, 2),
+                              "two_pass_bytes_per_layer": bm["sc_layer"],
+                              "kv_tokens_per_s": float(f"{tok * cfg.layers / (sc_ms / 1e3):.4g}"),
+                              "path": ("single read: one launch holds K on chip"
+                                       if wl.single_read else "two passes over K")},
+            "decode": {"ms_per_step": round(dec_ms, 4), "GBps": round(dec_gbs, 1),
+                       "pct_of_peak": round(100 * dec_gbs / PEAK_GBS, 2),
+                       "us_per_call": round(dec_call_us, 2),
+                       "kv_tokens_per_s": float(f"{tok * n_dec / (dec_ms / 1e3):.4g}"),
+                       "bytes_per_call": bm["dec_call"]},
+        },
+        "roofline": {"kernel": "k_decode_mfma (think_decode_attn chunk pass)",
+                     "bound": "hbm", "achieved": round(achieved, 1) if achieved else None,
+                     "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_GBS, 4) if achieved else None,
+                     "algorithmic_bytes_per_launch": bm["dec_call"],
+                     "launch_us": round(part_us, 2) if n_part else None,
+                     "launch_us_p10_p50_p90": part_pct,
+                     "timing": (f"HIP events on the launch stream around each of {n_part} "
+                                f"chunk-pass launches (one step's decode calls, repeated to at "
+                                f"least 64), after the timed steps")},
+        "near_ties": near,
+        "input_copies": wl.ncopies,
+    }
+    if extras:
+        app_us, app_bytes = append_time(cfg, torch, qdk, dev)
+        log(f"decode-time append: {app_us:.2f} us per call")
+        sep_us, fus_us = append_decode_time(wl, torch, qdk)
+        log(f"append+decode on layer 0: separate {sep_us:.2f} us, fused {fus_us:.2f} us per step")
+        rec["paths"]["append"] = {"us_per_call": round(app_us, 2), "bytes_per_call": app_bytes,
+                                  "note": "think_append_kv, timed apart from the step (the "
+                                          "workload's caches are full)"}
+        rec["paths"]["append_decode"] = {
+            "separate_us_per_step": round(sep_us, 2), "fused_us_per_step": round(fus_us, 2),
+            "note": "layer 0 in caches with 64 free rows: 64 steps of think_append_kv + "
+                    "think_decode_attn, then of think_append_decode_attn from the same lengths"}
+        pre = None
+        if cfg.batch == 1:
+            pw_us, ps_us, pc_us = prefill_time(wl, torch, qdk)
+            e = 2 if cfg.dtype == "bf16" else 4
+            K = tok * cfg.n_kv_heads * cfg.head_dim * e
+            Kt = tok * cfg.n_kv_heads * cfg.keep * e
+            Qw = cfg.obs_window * cfg.n_q_heads * cfg.head_dim * e
+            pre = {"write_us_per_layer": round(pw_us, 1),
+                   "write_GBps": round(4 * K / (pw_us * 1e-6) / 1e9, 1),
+                   "score_select_from_sums_us": round(ps_us, 2),
+                   "compact_us": round(pc_us, 1),
+                   "prune_after_prefill_GBps": round((K + Kt + Qw) / ((ps_us + pc_us) * 1e-6) / 1e9,
+                                                     1),
+                   "prune_after_prefill_pct_of_peak":
+                       round(100 * (K + Kt + Qw) / ((ps_us + pc_us) * 1e-6) / 1e9 / PEAK_GBS, 2),
+                   "note": "layer 0: prompt written in 8192-row chunks (reads and writes K and V: "
+                           "4|K| bytes) gathering the key sums; then scores+selection from the "
+                           "sums and compaction, |K| + |K_thin| + |Q_w| bytes (one read of K)"}
+            log(f"prefill-fused scoring: write {pw_us:.1f} us, score from sums {ps_us:.2f} us, "
+                f"compact {pc_us:.1f} us per layer")
+        rec["paths"]["prefill_fused_scoring"] = pre
+    return wl, rec
 
 
 def main():
@@ -467,88 +700,20 @@ def main():
         torch.cuda.synchronize()
         log(f"calibration copy of {args.calibrate_copy_mib} MiB done")
         del src, dst
-    wl = Workload(cfg, torch, qdk, dev)
-    wl.prepare_decode()
-    stream = torch.cuda.current_stream()
-    sp = ctypes.c_void_p(stream.cuda_stream)
-    bm = wl.bytes_model()
-    n_dec = cfg.decode_steps * cfg.layers
 
-    for _ in range(max(args.warmup, 1 if wl.ncopies > 1 else 0)):
-        for _ in range(wl.ncopies):              # every copy's thin cache is filled
-            wl.score_compact(sp)
-        wl.decode(sp)
-    torch.cuda.synchronize()
-    log("warmup done")
-
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        a, b, c = ev[k]
-        a.record(stream)
-        wl.score_compact(sp)
-        b.record(stream)
-        wl.decode(sp)
-        c.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    sc_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
-    dec_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
-    log(f"timed {args.steps} steps: {wall:.3f}s wall, score+compact {sc_ms:.3f} ms, "
-        f"decode {dec_ms:.3f} ms per step")
-
-    ms_per_step = wall / args.steps * 1e3
-    step_bytes = cfg.layers * bm["sc_layer"] + n_dec * bm["dec_call"]
-    value = step_bytes / (ms_per_step / 1e3) / 1e9
-    tok = bm["tokens"]
-    kv_tok_s = (tok * cfg.layers * (1 + cfg.decode_steps)) / (ms_per_step / 1e3)
-    sc_gbs = cfg.layers * bm["sc_layer"] / (sc_ms / 1e3) / 1e9
-    dec_gbs = n_dec * bm["dec_call"] / (dec_ms / 1e3) / 1e9
-    dec_call_us = dec_ms * 1e3 / n_dec
-    near = int(sum(int(e["tie"].sum().item()) for e in wl.layers))
-    # the dominant kernel's own launch duration, live, with HIP events (a
-    # separate pass after the timed region, so the events do not perturb it)
-    if args.no_kernel_timing:
-        part_us, n_part, part_pct = float("nan"), 0, None
-    else:
-        part_us, n_part, part_pct = wl.decode_kernel_times(sp, torch)
-        log(f"chunk-pass kernel: {part_us:.2f} us mean over {n_part} launches")
-    achieved = bm["dec_call"] / (part_us * 1e-6) / 1e9 if n_part else None
-    app_us, app_bytes = append_time(cfg, torch, qdk, dev)
-    log(f"decode-time append: {app_us:.2f} us per call")
-    sep_us, fus_us = append_decode_time(wl, torch, qdk)
-    log(f"append+decode on layer 0: separate {sep_us:.2f} us, fused {fus_us:.2f} us per step")
-    pre = None
-    if cfg.batch == 1:
-        pw_us, ps_us, pc_us = prefill_time(wl, torch, qdk)
-        e = 2 if cfg.dtype == "bf16" else 4
-        K = tok * cfg.n_kv_heads * cfg.head_dim * e
-        Kt = tok * cfg.n_kv_heads * cfg.keep * e
-        Qw = cfg.obs_window * cfg.n_q_heads * cfg.head_dim * e
-        pre = {"write_us_per_layer": round(pw_us, 1),
-               "write_GBps": round(4 * K / (pw_us * 1e-6) / 1e9, 1),
-               "score_select_from_sums_us": round(ps_us, 2),
-               "compact_us": round(pc_us, 1),
-               "prune_after_prefill_GBps": round((K + Kt + Qw) / ((ps_us + pc_us) * 1e-6) / 1e9, 1),
-               "prune_after_prefill_pct_of_peak":
-                   round(100 * (K + Kt + Qw) / ((ps_us + pc_us) * 1e-6) / 1e9 / PEAK_GBS, 2),
-               "note": "layer 0: prompt written in 8192-row chunks (reads and writes K and V: "
-                       "4|K| bytes) gathering the key sums; then scores+selection from the sums "
-                       "and compaction, |K| + |K_thin| + |Q_w| bytes (one read of K)"}
-        log(f"prefill-fused scoring: write {pw_us:.1f} us, score from sums {ps_us:.2f} us, "
-            f"compact {pc_us:.1f} us per layer")
+    wl, rec = measure(cfg, args, torch, qdk, dev, args.steps, args.warmup,
+                      extras=not args.no_extras)
     traffic, traffic_src = committed_traffic(cfg.name)
-
+    rec["roofline"]["traffic"] = traffic
+    rec["roofline"]["traffic_source"] = traffic_src
     result = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": rec["GBps"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 3),
+        "ms_per_step": round(rec["ms_per_step"], 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -558,57 +723,50 @@ def main():
                    "seq_len": cfg.seq_capacity, "n_q_heads": cfg.n_q_heads,
                    "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim,
                    "obs_window": cfg.obs_window, "keep": cfg.keep,
-                   "decode_steps": cfg.decode_steps, "valid_tokens_per_layer": tok},
-        "pct_of_peak": round(100 * value / PEAK_GBS, 2),
-        "value_note": ("bytes counted as two passes over K; the score+compact path read K once "
-                       "(effective bandwidth)" if wl.single_read else
-                       "algorithmic bytes of the path as run"),
-        "kv_tokens_per_s": float(f"{kv_tok_s:.4g}"),
-        "paths": {
-            "score_compact": {"ms_per_step": round(sc_ms, 3), "GBps": round(sc_gbs, 1),
-                              "pct_of_peak": round(100 * sc_gbs / PEAK_GBS, 2),
-                              "kv_tokens_per_s": float(f"{tok * cfg.layers / (sc_ms / 1e3):.4g}"),
-                              "bytes_per_layer": bm["sc_layer"],
-                              "single_read_bytes_per_layer": bm["sc_min_layer"],
-                              "path": ("single read: one launch holds K on chip"
-                                       if wl.single_read else "two passes over K"),
-                              "GBps_is_effective": bool(wl.single_read),
-                              "GBps_moved": round(cfg.layers * (bm["sc_min_layer"] if wl.single_read
-                                                                else bm["sc_layer"])
-                                                  / (sc_ms / 1e3) / 1e9, 1)},
-            "decode": {"ms_per_step": round(dec_ms, 3), "GBps": round(dec_gbs, 1),
-                       "pct_of_peak": round(100 * dec_gbs / PEAK_GBS, 2),
-                       "us_per_call": round(dec_call_us, 2),
-                       "kv_tokens_per_s": float(f"{tok * n_dec / (dec_ms / 1e3):.4g}"),
-                       "bytes_per_call": bm["dec_call"]},
-            "prefill_fused_scoring": pre,
-            "append": {"us_per_call": round(app_us, 2), "bytes_per_call": app_bytes,
-                       "note": "think_append_kv, timed apart from the step (the workload's "
-                               "caches are full)"},
-            "append_decode": {"separate_us_per_step": round(sep_us, 2),
-                              "fused_us_per_step": round(fus_us, 2),
-                              "note": "layer 0 in caches with 64 free rows: 64 steps of "
-                                      "think_append_kv + think_decode_attn, then of "
-                                      "think_append_decode_attn from the same lengths"},
-        },
-        "roofline": {"kernel": "k_decode_mfma (think_decode_attn chunk pass)",
-                     "bound": "hbm", "achieved": round(achieved, 1) if achieved else None,
-                     "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_GBS, 4) if achieved else None,
-                     "traffic": traffic,
-                     "algorithmic_bytes_per_launch": bm["dec_call"],
-                     "launch_us": round(part_us, 2) if n_part else None,
-                     "launch_us_p10_p50_p90": part_pct,
-                     "timing": (f"HIP events on the launch stream around each of {n_part} "
-                                f"chunk-pass launches (one step's decode calls, repeated to at "
-                                f"least 64), after the timed steps"),
-                     "traffic_source": traffic_src},
-        "near_ties": near,
-        "input_copies": wl.ncopies,
+                   "decode_steps": cfg.decode_steps,
+                   "valid_tokens_per_layer": int(wl.lens_host.sum())},
+        "pct_of_peak": rec["pct_of_peak"],
+        "value_note": ("HBM bytes the path as run moves per step / wall time; "
+                       "value_effective counts score+compact as two passes over K"),
+        "value_effective": rec["GBps_effective"],
+        "kv_tokens_per_s": rec["kv_tokens_per_s"],
+        "paths": rec["paths"],
+        "roofline": rec["roofline"],
+        "near_ties": rec["near_ties"],
+        "input_copies": rec["input_copies"],
     }
+    g0 = gpu_layer0(wl, torch)
+    ref = None
     if not args.no_cpu_baseline:
-        log("cpu baseline (oracle) ...")
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget_s)
+        log("cpu baseline (oracle, all host threads, then one thread) ...")
+        result["cpu_baseline"], ref = cpu_baseline(wl, args.cpu_budget_s)
+    elif args.parity:
+        _, ref = oracle_sample(wl, 0.0, len(os.sched_getaffinity(0)))
+    if ref is not None:
+        result["parity"] = parity(wl, g0, ref)
+        log(f"parity on layer 0 of {cfg.name}: {result['parity']}")
+    # the other workload the throughput target names, measured in the same run
+    also = [w for w in args.also.split(",") if w and w != cfg.name]
+    if also:
+        del wl
+        torch.cuda.empty_cache()
+        result["also"] = {}
+        for name in also:
+            c2 = kvsynth.CONFIGS[name]
+            wl2, r2 = measure(c2, args, torch, qdk, dev, args.also_steps, 3, extras=False)
+            g2 = gpu_layer0(wl2, torch)
+            if not args.no_cpu_baseline or args.parity:
+                _, ref2 = oracle_sample(wl2, 0.0, len(os.sched_getaffinity(0)))
+                r2["parity"] = parity(wl2, g2, ref2)
+                log(f"parity on layer 0 of {name}: {r2['parity']}")
+            r2["config"] = {"workload": c2.name, "layers": c2.layers, "batch": c2.batch,
+                            "seq_len": c2.seq_capacity, "n_q_heads": c2.n_q_heads,
+                            "n_kv_heads": c2.n_kv_heads, "head_dim": c2.head_dim,
+                            "obs_window": c2.obs_window, "keep": c2.keep,
+                            "decode_steps": c2.decode_steps, "steps": args.also_steps}
+            result["also"][name] = r2
+            del wl2
+            torch.cuda.empty_cache()
     print(json.dumps(result), flush=True)
 
 

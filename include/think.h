@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define THINK_ABI_VERSION 5
+#define THINK_ABI_VERSION 6
 
 #ifndef THINK_API
 #define THINK_API __attribute__((visibility("default")))
@@ -55,7 +55,8 @@ typedef enum {
     THINK_ERR_DTYPE = -4,       /* unknown dtype code */
     THINK_ERR_UNSUPPORTED = -5, /* valid, but outside what the kernels handle */
     THINK_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than required */
-    THINK_ERR_HIP = -7          /* a HIP launch failed; see think_last_hip_error */
+    THINK_ERR_HIP = -7,         /* a HIP launch failed; see think_last_hip_error */
+    THINK_ERR_WAIT = -8         /* a single-read launch gave up waiting: its outputs are invalid */
 } think_status;
 
 typedef enum { THINK_F32 = 0, THINK_BF16 = 1 } think_dtype;
@@ -161,8 +162,10 @@ THINK_API int think_compact_k(const think_dims *d, const void *k_cache, const in
  * workgroups of that launch wait for one another, so it needs every compute
  * unit to become free in time: it must not run concurrently with another
  * single-read launch or share the device with a kernel that never finishes.
- * Its waits are bounded (about 4 s), so a violation ends with wrong outputs
- * rather than a hang.
+ * Its waits are bounded (about 4 s), so a violation ends rather than hangs;
+ * the launch then records that it gave up, and think_score_compact_status
+ * reports it (THINK_ERR_WAIT: kept_idx, near_tie, scores and k_thin of that
+ * call are invalid).
  * Both paths give the same kept channels up to the near-tie flag (scores may
  * differ in the last fp32 place: the token sums are split differently) and,
  * for the same kept channels, the same k_thin bytes.
@@ -179,6 +182,22 @@ THINK_API int think_score_select_compact(const think_dims *d, const void *k_cach
                                          int32_t *kept_idx, int32_t *near_tie, void *k_thin,
                                          void *workspace, size_t workspace_bytes, void *stream);
 THINK_API size_t think_score_compact_workspace_bytes(const think_dims *d, int32_t keep);
+/* Outcome of the latest think_score_select_compact on `workspace` (same d,
+ * obs_window, keep and workspace as that call).  Waits for `stream`, then returns THINK_OK
+ * if its outputs are valid, or THINK_ERR_WAIT if its single-read launch gave
+ * up waiting (the one-launch-at-a-time rule above was broken); argument
+ * errors as for the call, THINK_ERR_HIP if the stream or the copy failed.  A
+ * shape that runs the two-pass kernels never waits: THINK_OK without touching
+ * the device.  Only meaningful after such a call on this workspace. */
+THINK_API int think_score_compact_status(const think_dims *d, int32_t obs_window, int32_t keep,
+                                         const void *workspace, size_t workspace_bytes,
+                                         void *stream);
+/* Test hook, not for production use: while `on` is nonzero, single-read
+ * launches enqueued from the calling thread wait for a tag that is never
+ * written and give up after a few polls, so that the give-up report can be
+ * tested without stalling the device.  Their outputs are invalid.  Returns the
+ * previous setting. */
+THINK_API int think_single_read_test_give_up(int on);
 /* 1 if think_score_select_compact takes the single-read launch for this shape
  * on the current device, 0 if it runs the two-pass kernels, negative status
  * for invalid dims or keep. */

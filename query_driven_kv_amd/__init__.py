@@ -22,7 +22,8 @@ __all__ = ["think_score", "think_score_select", "think_select", "think_compact_k
            "think_decode_attn_partial", "think_decode_attn_combine", "think_append_kv",
            "think_append_decode_attn", "think_k2_state_bytes", "think_prefill_write_kv", "think_score_select_k2",
            "think_score_select_compact", "think_score_compact_workspace_bytes",
-           "think_score_compact_single_read",
+           "think_score_compact_single_read", "think_score_compact_status",
+           "think_single_read_test_give_up",
            "think_keep_from_ratio", "think_score_workspace_bytes", "think_decode_workspace_bytes",
            "think_abi_version", "make_dims", "ThinkError", "think_dims", "LIB_PATH"]
 
@@ -49,6 +50,21 @@ def _dev(*ts):
 def _stream(stream):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _new(stream, *shape, dtype, device):
+    """A tensor this layer allocates for a call (output or workspace).  The
+    kernels run on `stream`; when that is not the current stream, the caching
+    allocator is told, so that the block is not handed to another allocation
+    while the call may still use it."""
+    t = torch.empty(*shape, dtype=dtype, device=device)
+    if stream is not None and stream != torch.cuda.current_stream(t.device):
+        t.record_stream(stream)
+    return t
+
+
+def _workspace(stream, nbytes, device):
+    return _new(stream, max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
 
 def _p(t):
@@ -89,6 +105,25 @@ def think_score_compact_single_read(dims, keep):
     return r
 
 
+def think_score_compact_status(dims, obs_window, keep, workspace, *, stream=None):
+    """Outcome of the latest think_score_select_compact on `workspace` (waits
+    for the stream): 0 (THINK_OK) if its outputs are valid, -8 (THINK_ERR_WAIT)
+    if its single-read launch gave up waiting.  Other errors raise."""
+    _dev(workspace)
+    r = _lib.lib.think_score_compact_status(
+        ctypes.byref(dims), int(obs_window), int(keep), _p(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    if r not in (0, -8):
+        _lib.check("think_score_compact_status", r)
+    return r
+
+
+def think_single_read_test_give_up(on):
+    """Test hook: while on, this thread's single-read launches give up every
+    wait (their outputs are invalid).  Returns the previous setting."""
+    return bool(_lib.lib.think_single_read_test_give_up(1 if on else 0))
+
+
 def _i32(t, name):
     if t.dtype != torch.int32:
         raise TypeError(f"{name} must be int32")
@@ -105,12 +140,12 @@ def think_score(k_cache, seq_lens, q_obs, *, scores=None, workspace=None, stream
         raise ValueError("shape or dtype mismatch between k_cache, q_obs and seq_lens")
     dims = make_dims(B, Hq, Hkv, D, S, _dtype_code(k_cache))
     if scores is None:
-        scores = torch.empty(B, Hkv, D, dtype=torch.float32, device=k_cache.device)
+        scores = _new(stream, B, Hkv, D, dtype=torch.float32, device=k_cache.device)
     elif scores.dtype != torch.float32 or tuple(scores.shape) != (B, Hkv, D):
         raise ValueError("scores must be float32 [B,Hkv,D]")
     need = think_score_workspace_bytes(dims)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=k_cache.device)
+        workspace = _workspace(stream, need, k_cache.device)
     _lib.check("think_score", _lib.lib.think_score(
         ctypes.byref(dims), _p(k_cache), _p(seq_lens), _p(q_obs), W, _p(scores), _p(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
@@ -130,14 +165,13 @@ def think_score_select(k_cache, seq_lens, q_obs, keep, *, scores=None, kept_idx=
     dims = make_dims(B, Hq, Hkv, D, S, _dtype_code(k_cache))
     dev = k_cache.device
     if scores is None:
-        scores = torch.empty(B, Hkv, D, dtype=torch.float32, device=dev)
+        scores = _new(stream, B, Hkv, D, dtype=torch.float32, device=dev)
     if kept_idx is None:
-        kept_idx = torch.empty(B, Hkv, max(int(keep), 0), dtype=torch.int32, device=dev)
+        kept_idx = _new(stream, B, Hkv, max(int(keep), 0), dtype=torch.int32, device=dev)
     if near_tie is None:
-        near_tie = torch.empty(B, Hkv, dtype=torch.int32, device=dev)
+        near_tie = _new(stream, B, Hkv, dtype=torch.int32, device=dev)
     if workspace is None:
-        workspace = torch.empty(max(think_score_workspace_bytes(dims), 16), dtype=torch.uint8,
-                                device=dev)
+        workspace = _workspace(stream, think_score_workspace_bytes(dims), dev)
     _lib.check("think_score_select", _lib.lib.think_score_select(
         ctypes.byref(dims), _p(k_cache), _p(seq_lens), _p(q_obs), W, int(keep), _p(scores),
         _p(kept_idx), _p(near_tie), _p(workspace), workspace.numel() * workspace.element_size(),
@@ -153,9 +187,10 @@ def think_select(scores, keep, *, kept_idx=None, near_tie=None, want_near_tie=Tr
     B, Hkv, D = scores.shape
     dims = make_dims(B, Hkv, Hkv, D, 1, THINK_F32)
     if kept_idx is None:
-        kept_idx = torch.empty(B, Hkv, max(int(keep), 0), dtype=torch.int32, device=scores.device)
+        kept_idx = _new(stream, B, Hkv, max(int(keep), 0), dtype=torch.int32,
+                        device=scores.device)
     if want_near_tie and near_tie is None:
-        near_tie = torch.empty(B, Hkv, dtype=torch.int32, device=scores.device)
+        near_tie = _new(stream, B, Hkv, dtype=torch.int32, device=scores.device)
     _lib.check("think_select", _lib.lib.think_select(
         ctypes.byref(dims), _p(scores), int(keep), _p(kept_idx), _p(near_tie), _stream(stream)))
     return kept_idx, near_tie
@@ -173,7 +208,7 @@ def think_compact_k(k_cache, seq_lens, kept_idx, *, k_thin=None, stream=None):
         raise ValueError("kept_idx must be [B,Hkv,keep]")
     dims = make_dims(B, Hkv, Hkv, D, S, _dtype_code(k_cache))
     if k_thin is None:
-        k_thin = torch.empty(B, S, Hkv, keep, dtype=k_cache.dtype, device=k_cache.device)
+        k_thin = _new(stream, B, S, Hkv, keep, dtype=k_cache.dtype, device=k_cache.device)
     elif tuple(k_thin.shape) != (B, S, Hkv, keep) or k_thin.dtype != k_cache.dtype:
         raise ValueError("k_thin must be [B,S_cap,Hkv,keep] of the cache dtype")
     _lib.check("think_compact_k", _lib.lib.think_compact_k(
@@ -183,10 +218,13 @@ def think_compact_k(k_cache, seq_lens, kept_idx, *, k_thin=None, stream=None):
 
 
 def think_score_select_compact(k_cache, seq_lens, q_obs, keep, *, scores=None, kept_idx=None,
-                               near_tie=None, k_thin=None, workspace=None, stream=None):
+                               near_tie=None, k_thin=None, workspace=None, stream=None,
+                               check_status=False):
     """Stages (a)+(b)+(c) in one call (one read of K when it fits on chip).
     Returns (scores fp32 [B,Hkv,D], kept_idx int32 [B,Hkv,keep], near_tie
-    int32 [B,Hkv], k_thin [B,S_cap,Hkv,keep])."""
+    int32 [B,Hkv], k_thin [B,S_cap,Hkv,keep]).  check_status=True waits for
+    the call and raises ThinkError (THINK_ERR_WAIT) if its single-read launch
+    gave up waiting."""
     _dev(k_cache, seq_lens, q_obs, scores, kept_idx, near_tie, k_thin, workspace)
     _i32(seq_lens, "seq_lens")
     B, S, Hkv, D = k_cache.shape
@@ -197,22 +235,24 @@ def think_score_select_compact(k_cache, seq_lens, q_obs, keep, *, scores=None, k
     dev = k_cache.device
     keep = int(keep)
     if scores is None:
-        scores = torch.empty(B, Hkv, D, dtype=torch.float32, device=dev)
+        scores = _new(stream, B, Hkv, D, dtype=torch.float32, device=dev)
     if kept_idx is None:
-        kept_idx = torch.empty(B, Hkv, max(keep, 0), dtype=torch.int32, device=dev)
+        kept_idx = _new(stream, B, Hkv, max(keep, 0), dtype=torch.int32, device=dev)
     if near_tie is None:
-        near_tie = torch.empty(B, Hkv, dtype=torch.int32, device=dev)
+        near_tie = _new(stream, B, Hkv, dtype=torch.int32, device=dev)
     if k_thin is None:
-        k_thin = torch.empty(B, S, Hkv, max(keep, 0), dtype=k_cache.dtype, device=dev)
+        k_thin = _new(stream, B, S, Hkv, max(keep, 0), dtype=k_cache.dtype, device=dev)
     elif tuple(k_thin.shape) != (B, S, Hkv, keep) or k_thin.dtype != k_cache.dtype:
         raise ValueError("k_thin must be [B,S_cap,Hkv,keep] of the cache dtype")
     if workspace is None:
-        workspace = torch.empty(max(think_score_compact_workspace_bytes(dims, keep), 16),
-                                dtype=torch.uint8, device=dev)
+        workspace = _workspace(stream, think_score_compact_workspace_bytes(dims, keep), dev)
     _lib.check("think_score_select_compact", _lib.lib.think_score_select_compact(
         ctypes.byref(dims), _p(k_cache), _p(seq_lens), _p(q_obs), W, keep, _p(scores),
         _p(kept_idx), _p(near_tie), _p(k_thin), _p(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+    if check_status:
+        _lib.check("think_score_select_compact",
+                   think_score_compact_status(dims, W, keep, workspace, stream=stream))
     return scores, kept_idx, near_tie, k_thin
 
 
@@ -230,10 +270,10 @@ def think_decode_attn(q, k_thin, v_cache, seq_lens, kept_idx, softmax_scale, *, 
         raise ValueError("shape or dtype mismatch between q, k_thin, v_cache and kept_idx")
     dims = make_dims(B, Hq, Hkv, D, S, _dtype_code(q))
     if out is None:
-        out = torch.empty(B, Hq, D, dtype=q.dtype, device=q.device)
+        out = _new(stream, B, Hq, D, dtype=q.dtype, device=q.device)
     need = think_decode_workspace_bytes(dims, keep)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = _workspace(stream, need, q.device)
     _lib.check("think_decode_attn", _lib.lib.think_decode_attn(
         ctypes.byref(dims), _p(q), _p(k_thin), _p(v_cache), _p(seq_lens), _p(kept_idx), int(keep),
         float(softmax_scale), _p(out), _p(workspace), workspace.numel() * workspace.element_size(),
@@ -312,10 +352,10 @@ def think_append_decode_attn(q, k_new, v_new, k_thin, v_cache, seq_lens, kept_id
                          "kept_idx")
     dims = make_dims(B, Hq, Hkv, D, S, _dtype_code(q))
     if out is None:
-        out = torch.empty(B, Hq, D, dtype=q.dtype, device=q.device)
+        out = _new(stream, B, Hq, D, dtype=q.dtype, device=q.device)
     need = think_decode_workspace_bytes(dims, keep)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = _workspace(stream, need, q.device)
     _lib.check("think_append_decode_attn", _lib.lib.think_append_decode_attn(
         ctypes.byref(dims), _p(q), _p(k_new), _p(v_new), _p(k_thin), _p(v_cache), _p(seq_lens),
         _p(kept_idx), int(keep), float(softmax_scale), _p(out), _p(workspace),
@@ -359,12 +399,12 @@ def think_score_select_k2(dims, k2_state, q_obs, keep=None, *, scores=None, kept
         raise ValueError("q_obs must be [B,W,Hq,D] of the dims' dtype")
     dev = q_obs.device
     if scores is None:
-        scores = torch.empty(B, Hkv, D, dtype=torch.float32, device=dev)
+        scores = _new(stream, B, Hkv, D, dtype=torch.float32, device=dev)
     if keep is not None:
         if kept_idx is None:
-            kept_idx = torch.empty(B, Hkv, keep, dtype=torch.int32, device=dev)
+            kept_idx = _new(stream, B, Hkv, keep, dtype=torch.int32, device=dev)
         if near_tie is None:
-            near_tie = torch.empty(B, Hkv, dtype=torch.int32, device=dev)
+            near_tie = _new(stream, B, Hkv, dtype=torch.int32, device=dev)
     _lib.check("think_score_select_k2", _lib.lib.think_score_select_k2(
         ctypes.byref(dims), _p(k2_state), k2_state.numel() * k2_state.element_size(), _p(q_obs),
         int(W), int(keep or 0), _p(scores), _p(kept_idx), _p(near_tie), _stream(stream)))

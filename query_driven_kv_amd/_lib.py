@@ -12,7 +12,7 @@ _SO = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libthinkkv.so")
 THINK_F32, THINK_BF16 = 0, 1
 STATUS = {0: "THINK_OK", -1: "THINK_ERR_NULL", -2: "THINK_ERR_SHAPE", -3: "THINK_ERR_KEEP",
           -4: "THINK_ERR_DTYPE", -5: "THINK_ERR_UNSUPPORTED", -6: "THINK_ERR_WORKSPACE",
-          -7: "THINK_ERR_HIP"}
+          -7: "THINK_ERR_HIP", -8: "THINK_ERR_WAIT"}
 
 # every function include/think.h declares
 EXPORTS = ("think_abi_version", "think_keep_from_ratio", "think_score_workspace_bytes",
@@ -23,6 +23,7 @@ EXPORTS = ("think_abi_version", "think_keep_from_ratio", "think_score_workspace_
            "think_prefill_write_kv",
            "think_score_select_k2", "think_score_select_compact",
            "think_score_compact_workspace_bytes", "think_score_compact_single_read",
+           "think_score_compact_status", "think_single_read_test_give_up",
            "think_status_string", "think_last_hip_error")
 
 
@@ -81,6 +82,10 @@ def _load():
     l.think_score_compact_workspace_bytes.restype = sz
     l.think_score_compact_single_read.argtypes = [pd, i32]
     l.think_score_compact_single_read.restype = ctypes.c_int
+    l.think_score_compact_status.argtypes = [pd, i32, i32, vp, sz, vp]
+    l.think_score_compact_status.restype = ctypes.c_int
+    l.think_single_read_test_give_up.argtypes = [ctypes.c_int]
+    l.think_single_read_test_give_up.restype = ctypes.c_int
     l.think_status_string.argtypes = [ctypes.c_int]
     l.think_status_string.restype = ctypes.c_char_p
     l.think_last_hip_error.restype = ctypes.c_int

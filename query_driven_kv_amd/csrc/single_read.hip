@@ -76,14 +76,15 @@ __device__ __forceinline__ void signal_flag(unsigned long long* f, unsigned long
 // on the current value (a plain load can return a copy cached on this
 // chiplet); one acquire fence for the workgroup after the waits.
 __device__ __forceinline__ void wait_flags(unsigned long long* f, int n,
-                                           unsigned long long tag, unsigned* err) {
+                                           unsigned long long tag, unsigned long long want,
+                                           uint32_t limit, unsigned long long* err) {
     for (int i = threadIdx.x; i < n; i += blockDim.x) {
         for (uint32_t spin = 0;; ++spin) {
             if (__hip_atomic_fetch_add(f + i, 0ull, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT) == tag)
+                                       __HIP_MEMORY_SCOPE_AGENT) == want)
                 break;
-            if (spin == kSrSpinLimit) {
-                __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (spin >= limit) {
+                __hip_atomic_store(err, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 break;
             }
             __builtin_amdgcn_s_sleep(2);
@@ -106,9 +107,11 @@ struct SrParams {
     void* k_thin;              // [B][S_cap][Hkv][keep]
     unsigned long long* tile_done;   // [nwg] flags
     unsigned long long* selected;    // [B][Hkv][ceil(D/16)] tag << 16 | 16 mask bits
-    unsigned* err;                   // set if a wait ran out
+    unsigned long long* err;         // the tag of a launch whose wait ran out, else 0
     unsigned long long* gen;         // launch generation, advanced by every launch
     unsigned long long tag;          // per call, low 24 bits nonzero (frozen in a captured graph)
+    unsigned long long want_xor;     // 0; nonzero only to test the give-up report (no wait matches)
+    uint32_t spin_limit;             // polls before a wait gives up
     int s_cap, nvec, rpw, wps, nb, W, nqv, Hq, Hkv, D, keep;
 };
 
@@ -133,7 +136,6 @@ __global__ __launch_bounds__(kSrThreads) void k_score_compact_resident(SrParams 
     const int t0 = part * p.rpw;
     const int len = clamp_len(p.seq_lens, b, p.s_cap);
     const int nt = max(0, min(p.rpw, len - t0));  // valid rows of this tile
-    if (w == 0 && tid == 0) *p.err = 0u;          // set only if a wait runs out
     // the flags' 48-bit tag: the workspace's launch generation (which
     // workgroup 0 advances once every workgroup has read it) above the call's
     // 24-bit value.  Launches on one workspace differ in the generation, so
@@ -142,6 +144,19 @@ __global__ __launch_bounds__(kSrThreads) void k_score_compact_resident(SrParams 
     const unsigned long long gen =
             __hip_atomic_load(p.gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const unsigned long long tag = ((gen & 0xffffffull) << 24) | (p.tag & 0xffffffull);
+    const unsigned long long want = tag ^ p.want_xor;
+    // The error word holds the tag of a launch whose wait ran out.  Workgroup 0
+    // clears whatever an earlier launch left, unless a workgroup of this launch
+    // has already reported (possible only if workgroup 0 started late), so the
+    // word describes the latest launch on the workspace.
+    if (w == 0 && tid == 0) {
+        const unsigned long long e =
+                __hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        unsigned long long ex = e;
+        if (e != tag)
+            __hip_atomic_compare_exchange_strong(p.err, &ex, 0ull, __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 
     // ---- phase 1: the tile into registers (vector tid + k*512 of the tile;
     // nvec divides 512, so every vector of a thread is in column tid % nvec)
@@ -237,7 +252,7 @@ __global__ __launch_bounds__(kSrThreads) void k_score_compact_resident(SrParams 
 
     // ---- phase 2: scores and selection, one workgroup per (b, kv)
     if (w < p.nb * p.Hkv) {
-        wait_flags(p.tile_done, nwg, tag, p.err);
+        wait_flags(p.tile_done, nwg, tag, want, p.spin_limit, p.err);
         // every workgroup has stored its flag, so every one has read gen
         if (w == 0 && tid == 0)
             __hip_atomic_store(p.gen, gen + 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -327,9 +342,9 @@ __global__ __launch_bounds__(kSrThreads) void k_score_compact_resident(SrParams 
             for (uint32_t spin = 0;; ++spin) {
                 x = __hip_atomic_fetch_add(words + i, 0ull, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
-                if ((x >> 16) == tag) break;
-                if (spin == kSrSpinLimit) {
-                    __hip_atomic_store(p.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if ((x >> 16) == want) break;
+                if (spin >= p.spin_limit) {
+                    __hip_atomic_store(p.err, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     break;
                 }
                 __builtin_amdgcn_s_sleep(2);
@@ -456,6 +471,10 @@ const void* sr_kernel_for(int dtype, int nv) {
     return nullptr;
 }
 
+// test hook (think_single_read_test_give_up): this thread's launches wait for
+// a tag nobody writes and give up after a few polls
+thread_local bool g_sr_test_give_up = false;
+
 // the call's share of the tag: a process-wide counter seeded from the clock,
 // 24 bits, never 0
 unsigned long long next_tag() {
@@ -469,6 +488,8 @@ unsigned long long next_tag() {
 
 }  // namespace
 
+void set_single_read_test_give_up(bool on) { g_sr_test_give_up = on; }
+
 SingleReadGeom single_read_geom(const think_dims& d, int keep) {
     SingleReadGeom g{};
     const int e = elem_bytes(d.dtype);
@@ -480,9 +501,10 @@ SingleReadGeom single_read_geom(const think_dims& d, int keep) {
                    ((size_t)d.batch * d.n_q_heads * d.head_dim * sizeof(double) + 15) / 16 * 16;
     // tile flags [kSrMaxWorkgroups], mask words [B][Hkv][ceil(D/16)], the error
     // word and the launch generation
-    g.ws_bytes = g.bar_offset +
-                 ((size_t)kSrMaxWorkgroups +
-                  (size_t)d.batch * d.n_kv_heads * ((d.head_dim + 15) / 16)) * 8 + 16;
+    g.err_offset = g.bar_offset +
+                   ((size_t)kSrMaxWorkgroups +
+                    (size_t)d.batch * d.n_kv_heads * ((d.head_dim + 15) / 16)) * 8;
+    g.ws_bytes = g.err_offset + 16;
     // shape conditions of the kernel (the device's share is decided at launch)
     g.shape_ok = nvec <= kSrThreads && kSrThreads % nvec == 0 &&
                  (d.n_q_heads / d.n_kv_heads) * d.head_dim <= 4096 &&
@@ -542,10 +564,14 @@ hipError_t launch_single_read(const think_dims& d, const SingleReadGeom& g, cons
     p.k_thin = k_thin;
     p.tile_done = reinterpret_cast<unsigned long long*>(ws + g.bar_offset);
     p.selected = p.tile_done + kSrMaxWorkgroups;
-    p.err = reinterpret_cast<unsigned*>(p.selected + (size_t)d.batch * d.n_kv_heads *
-                                                          ((d.head_dim + 15) / 16));
-    p.gen = reinterpret_cast<unsigned long long*>(p.err) + 1;
+    p.err = p.selected + (size_t)d.batch * d.n_kv_heads * ((d.head_dim + 15) / 16);
+    p.gen = p.err + 1;
     p.tag = next_tag();
+    p.spin_limit = kSrSpinLimit;
+    if (g_sr_test_give_up) {      // test hook: every wait runs out after a few polls
+        p.want_xor = 1ull << 47;
+        p.spin_limit = 4;
+    }
     p.s_cap = d.seq_capacity;
     p.nvec = d.n_kv_heads * d.head_dim * elem_bytes(d.dtype) / 16;
     p.rpw = pl.rpw;

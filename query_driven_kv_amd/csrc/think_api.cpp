@@ -132,6 +132,45 @@ int think_score_compact_single_read(const think_dims* d, int32_t keep) {
     return thinkkv::single_read_plan(*d, keep, thinkkv::single_read_geom(*d, keep), &pl) ? 1 : 0;
 }
 
+namespace {
+// the window rows of the single-read launch are read through one 32-bit buffer range
+bool window_fits(const think_dims* d, int32_t obs_window) {
+    return (int64_t)d->batch * obs_window * d->n_q_heads * d->head_dim *
+                   thinkkv::elem_bytes(d->dtype) < ((int64_t)1 << 31);
+}
+}  // namespace
+
+int think_score_compact_status(const think_dims* d, int32_t obs_window, int32_t keep,
+                               const void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_dims(d);
+    if (st != THINK_OK) return st;
+    if (obs_window < 1) return THINK_ERR_SHAPE;
+    if (keep < 1 || keep > d->head_dim) return THINK_ERR_KEEP;
+    const thinkkv::SingleReadGeom sg = thinkkv::single_read_geom(*d, keep);
+    const thinkkv::ScoreGeom g = thinkkv::score_geom(*d);
+    const size_t need = g.ws_bytes > sg.ws_bytes ? g.ws_bytes : sg.ws_bytes;
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return THINK_ERR_WORKSPACE;
+    thinkkv::SrPlan pl;
+    if (!window_fits(d, obs_window) || !thinkkv::single_read_plan(*d, keep, sg, &pl))
+        return THINK_OK;
+    hipStream_t s = (hipStream_t)stream;
+    unsigned long long err = 0;
+    st = hip_status(hipMemcpyAsync(&err, (const char*)workspace + sg.err_offset, sizeof(err),
+                                   hipMemcpyDeviceToHost, s));
+    if (st != THINK_OK) return st;
+    st = hip_status(hipStreamSynchronize(s));
+    if (st != THINK_OK) return st;
+    return err ? THINK_ERR_WAIT : THINK_OK;
+}
+
+int think_single_read_test_give_up(int on) {
+    static thread_local int cur = 0;
+    const int prev = cur;
+    cur = on != 0;
+    thinkkv::set_single_read_test_give_up(cur != 0);
+    return prev;
+}
+
 int think_score_select_compact(const think_dims* d, const void* k_cache, const int32_t* seq_lens,
                                const void* q_obs, int32_t obs_window, int32_t keep,
                                float* scores, int32_t* kept_idx, int32_t* near_tie,
@@ -150,10 +189,7 @@ int think_score_select_compact(const think_dims* d, const void* k_cache, const i
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return THINK_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     thinkkv::SrPlan pl;
-    // the window rows are read through one 32-bit buffer range
-    const bool q_fits = (int64_t)d->batch * obs_window * d->n_q_heads * d->head_dim *
-                                thinkkv::elem_bytes(d->dtype) < ((int64_t)1 << 31);
-    if (q_fits && thinkkv::single_read_plan(*d, keep, sg, &pl))
+    if (window_fits(d, obs_window) && thinkkv::single_read_plan(*d, keep, sg, &pl))
         return hip_status(thinkkv::launch_single_read(*d, sg, pl, k_cache, seq_lens,
                                                       q_obs, obs_window, scores, keep, kept_idx,
                                                       near_tie, k_thin, workspace, s));
@@ -311,6 +347,7 @@ const char* think_status_string(int status) {
         case THINK_ERR_UNSUPPORTED: return "shape, alignment or size outside what the kernels handle";
         case THINK_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
         case THINK_ERR_HIP: return "HIP launch failed";
+        case THINK_ERR_WAIT: return "a single-read launch gave up waiting; its outputs are invalid";
         default: return "unknown status";
     }
 }

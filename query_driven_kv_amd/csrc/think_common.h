@@ -222,6 +222,7 @@ struct SingleReadGeom {
     size_t part_bytes;
     size_t q2_offset;
     size_t bar_offset;
+    size_t err_offset;  // 64-bit word: the tag of the latest launch if one of its waits ran out
     size_t ws_bytes;
     bool shape_ok;     // the shape suits the kernel (the device decides the rest)
 };
@@ -232,6 +233,8 @@ struct SrPlan {
     size_t lds;        // dynamic LDS bytes
 };
 SingleReadGeom single_read_geom(const think_dims& d, int keep);
+// test hook: this thread's single-read launches give up every wait
+void set_single_read_test_give_up(bool on);
 bool single_read_plan(const think_dims& d, int keep, const SingleReadGeom& g, SrPlan* plan);
 hipError_t launch_single_read(const think_dims& d, const SingleReadGeom& g, const SrPlan& plan,
                               const void* k_cache, const int32_t* seq_lens,

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_header_declarations_are_all_exported(L):
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 23
     assert sorted(L.EXPORTS) == names
     so = ctypes.CDLL(L.LIB_PATH)
     for n in names:
@@ -42,7 +42,7 @@ def test_only_the_abi_is_exported(L):
 
 def test_version_and_keep_rounding(L):
     lib = L.lib
-    assert lib.think_abi_version() == 5
+    assert lib.think_abi_version() == 6
     assert [lib.think_keep_from_ratio(128, r) for r in (0.4, 0.6, 0.5)] == [77, 51, 64]
     assert lib.think_keep_from_ratio(16, 0.5) == 8
     assert lib.think_keep_from_ratio(128, 0.0) == 128
@@ -255,8 +255,35 @@ def test_null_keep_window_workspace_and_alignment(L):
                                   16, None) == -6
 
 
+def test_score_compact_status_validation(L):
+    """The give-up query checks its arguments like the call it reports on and
+    never touches the device for a bad argument."""
+    lib = L.lib
+    d = dims(L)
+    big = 1 << 30
+    assert lib.think_score_compact_status(None, 32, 8, FAKE, big, None) == -1
+    assert lib.think_score_compact_status(ctypes.byref(d), 0, 8, FAKE, big, None) == -2
+    assert lib.think_score_compact_status(ctypes.byref(d), 32, 0, FAKE, big, None) == -3
+    assert lib.think_score_compact_status(ctypes.byref(d), 32, 8, None, big, None) == -6
+    assert lib.think_score_compact_status(ctypes.byref(d), 32, 8, FAKE, 16, None) == -6
+    assert lib.think_score_compact_status(ctypes.byref(dims(L, Hq=30)), 32, 8, FAKE, big,
+                                          None) == -2
+
+
+def test_single_read_test_hook_is_per_thread(L):
+    import threading
+    lib = L.lib
+    assert lib.think_single_read_test_give_up(1) == 0
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(lib.think_single_read_test_give_up(0)))
+    t.start()
+    t.join()
+    assert seen == [0]                                    # another thread: its own setting
+    assert lib.think_single_read_test_give_up(0) == 1
+
+
 def test_status_strings(L):
-    for code in range(-7, 1):
+    for code in range(-8, 1):
         assert L.lib.think_status_string(code)
     assert L.lib.think_status_string(-99) == b"unknown status"
     assert L.lib.think_last_hip_error() == 0

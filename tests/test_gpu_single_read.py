@@ -55,6 +55,7 @@ def check_single_read(cfg, L, keep, label, expect_single):
     gen = torch.Generator(device="cpu").manual_seed(B * 7919 + S)
     ws = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=gen).to(k.device)
     g = _run(qdk, k, lens_d, qo, keep, ws)
+    assert qdk.think_score_compact_status(dims, cfg.obs_window, keep, ws) == 0, "wait gave up"
     lens = L["seq_lens"]
     # (i)
     ref_s = oracle.score(L["k_cache"], lens, L["q_obs"])
@@ -181,3 +182,49 @@ def test_random_shapes():
                  keep=keep, dtype=dtype, obs_window=int(rng.integers(1, 65)))
         cfg, L, _ = _custom(200 + case, lens, **c)
         check_single_read(cfg, L, keep, f"random{case}", _fits(c))
+
+
+def test_give_up_is_reported_and_cleared():
+    """A single-read launch whose waits give up says so through
+    think_score_compact_status; the next launch on the same workspace clears the
+    report and gives the normal result.  The give-up is forced from the host
+    (the test hook makes every wait look for a tag that is never written and stop
+    after a few polls), so every workgroup still finishes normally."""
+    qdk = _qdk()
+    cfg = kvsynth.CONFIGS["mistral-7b-gqa-32k"]
+    L = kvsynth.make_layer(cfg, 0)
+    k, lens_d, qo = to_dev(L["k_cache"]), to_dev(L["seq_lens"]), to_dev(L["q_obs"])
+    B, S, Hkv, D = k.shape
+    dims = qdk.make_dims(B, cfg.n_q_heads, Hkv, D, S, qdk.THINK_BF16)
+    assert qdk.think_score_compact_single_read(dims, cfg.keep) == 1
+    ws = torch.zeros(qdk.think_score_compact_workspace_bytes(dims, cfg.keep), dtype=torch.uint8,
+                     device=k.device)
+    good = _run(qdk, k, lens_d, qo, cfg.keep, ws)
+    assert qdk.think_score_compact_status(dims, cfg.obs_window, cfg.keep, ws) == 0
+    print("[single-read] give-up: forcing every wait to run out", flush=True)
+    prev = qdk.think_single_read_test_give_up(True)
+    try:
+        _run(qdk, k, lens_d, qo, cfg.keep, ws)
+    finally:
+        qdk.think_single_read_test_give_up(prev)
+    assert qdk.think_score_compact_status(dims, cfg.obs_window, cfg.keep, ws) == -8
+    prev = qdk.think_single_read_test_give_up(True)
+    try:
+        with pytest.raises(qdk.ThinkError) as ei:
+            qdk.think_score_select_compact(k, lens_d, qo, cfg.keep, workspace=ws,
+                                           check_status=True)
+    finally:
+        qdk.think_single_read_test_give_up(prev)
+    assert ei.value.status == -8
+    again = _run(qdk, k, lens_d, qo, cfg.keep, ws)
+    assert qdk.think_score_compact_status(dims, cfg.obs_window, cfg.keep, ws) == 0
+    for key in good:
+        np.testing.assert_array_equal(good[key].view(np.uint8), again[key].view(np.uint8))
+    # a two-pass shape never waits
+    c2 = kvsynth.CONFIGS["batched-ragged-16k"]
+    d2 = qdk.make_dims(c2.batch, c2.n_q_heads, c2.n_kv_heads, c2.head_dim, c2.seq_capacity,
+                       qdk.THINK_BF16)
+    assert qdk.think_score_compact_single_read(d2, c2.keep) == 0
+    ws2 = torch.zeros(qdk.think_score_compact_workspace_bytes(d2, c2.keep), dtype=torch.uint8,
+                      device=k.device)
+    assert qdk.think_score_compact_status(d2, c2.obs_window, c2.keep, ws2) == 0
