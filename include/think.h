@@ -227,6 +227,23 @@ THINK_API int think_decode_attn(const think_dims *d, const void *q, const void *
                       size_t workspace_bytes, void *stream);
 
 /*
+ * think_decode_attn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and result (bitwise), with no workspace argument.  The
+ * partial records live in a scratch array of 8 MiB that the library holds on
+ * every GPU it runs on, from that GPU's first such call until the process
+ * ends; the call itself allocates nothing.  All calls on one GPU share that
+ * array, so calls that overlap in time on one GPU (other streams, other host
+ * threads) race and must be ordered by the caller.  Returns THINK_ERR_WORKSPACE
+ * when think_decode_workspace_bytes(d, keep) exceeds 8 MiB (then use
+ * think_decode_attn); other errors as for think_decode_attn.
+ */
+THINK_API int think_decode_attn_static(const think_dims *d, const void *q, const void *k_thin,
+                                       const void *v_cache, const int32_t *seq_lens,
+                                       const int32_t *kept_idx, int32_t keep,
+                                       float softmax_scale, void *out, void *stream);
+
+/*
  * Split-phase form of think_decode_attn, same arguments and workspace.
  * think_decode_attn_partial runs the chunk pass: every (b, kv head, token
  * chunk) writes one partial softmax record per query head (running max,

@@ -18,7 +18,8 @@ STATUS = {0: "THINK_OK", -1: "THINK_ERR_NULL", -2: "THINK_ERR_SHAPE", -3: "THINK
 EXPORTS = ("think_abi_version", "think_keep_from_ratio", "think_score_workspace_bytes",
            "think_decode_workspace_bytes", "think_score", "think_score_select", "think_select",
            "think_compact_k",
-           "think_decode_attn", "think_decode_attn_partial", "think_decode_attn_combine",
+           "think_decode_attn", "think_decode_attn_static", "think_decode_attn_partial",
+           "think_decode_attn_combine",
            "think_append_kv", "think_append_decode_attn", "think_k2_state_bytes",
            "think_prefill_write_kv",
            "think_score_select_k2", "think_score_select_compact",
@@ -68,6 +69,7 @@ def _load():
     l.think_select.argtypes = [pd, vp, i32, vp, vp, vp]
     l.think_compact_k.argtypes = [pd, vp, vp, vp, i32, vp, vp]
     l.think_decode_attn.argtypes = [pd, vp, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp, sz, vp]
+    l.think_decode_attn_static.argtypes = [pd, vp, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp]
     l.think_decode_attn_partial.argtypes = [pd, vp, vp, vp, vp, vp, i32, ctypes.c_float, vp, sz, vp]
     l.think_decode_attn_combine.argtypes = [pd, vp, i32, vp, vp, sz, vp]
     l.think_append_kv.argtypes = [pd, vp, vp, vp, vp, i32, vp, vp, vp]
@@ -90,7 +92,7 @@ def _load():
     l.think_status_string.restype = ctypes.c_char_p
     l.think_last_hip_error.restype = ctypes.c_int
     for name in ("think_score", "think_score_select", "think_select", "think_compact_k",
-                 "think_decode_attn",
+                 "think_decode_attn", "think_decode_attn_static",
                  "think_decode_attn_partial", "think_decode_attn_combine", "think_append_kv",
                  "think_append_decode_attn",
                  "think_prefill_write_kv", "think_score_select_k2", "think_score_select_compact"):

@@ -17,11 +17,48 @@
 // This file holds the general kernel (any dtype, any keep, G <= 16) and the
 // combine kernel.  The bf16 matrix-core kernel for the bandwidth-critical
 // shapes is in decode_mfma.hip and writes the same partial records.
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "think_common.h"
 
 namespace thinkkv {
+
+// Scratch of the allocation-free decode (think_decode_attn_static): the chunk
+// pass's partial records and the stashed lengths live in this array instead of
+// a caller workspace.  Each GPU holds its own copy for the life of the
+// process; every call on a GPU shares it and leaves its contents behind (the
+// records are written before they are read, so nothing needs clearing), so
+// calls that overlap in time on one GPU race.  In host code the name is only a
+// stand-in: kernels take the device address that hipGetSymbolAddress returns
+// for the current device, fetched once per device.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 256;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t static_scratch(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lk(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
+}
 
 // defined in decode_mfma.hip
 bool mfma_decode_supported(const think_dims& d, int keep);

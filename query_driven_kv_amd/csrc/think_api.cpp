@@ -243,6 +243,30 @@ int think_decode_attn(const think_dims* d, const void* q, const void* k_thin,
                                                      nullptr, (hipStream_t)stream));
 }
 
+int think_decode_attn_static(const think_dims* d, const void* q, const void* k_thin,
+                             const void* v_cache, const int32_t* seq_lens,
+                             const int32_t* kept_idx, int32_t keep, float softmax_scale,
+                             void* out, void* stream) {
+    // the validation of think_decode_attn, with the scratch array standing in
+    // for the workspace
+    int st = check_dims(d);
+    if (st != THINK_OK) return st;
+    if (!seq_lens || !q || !k_thin || !v_cache || !kept_idx || !out) return THINK_ERR_NULL;
+    if (keep < 1 || keep > d->head_dim) return THINK_ERR_KEEP;
+    if (!aligned16(k_thin) || !aligned16(v_cache) || !aligned16(q)) return THINK_ERR_UNSUPPORTED;
+    const thinkkv::DecodeGeom g = thinkkv::decode_geom(*d, keep);
+    if (g.ws_bytes > thinkkv::kStaticScratchBytes) return THINK_ERR_WORKSPACE;
+    void* ws = nullptr;
+    st = hip_status(thinkkv::static_scratch(&ws));
+    if (st != THINK_OK) return st;
+    st = hip_status(thinkkv::launch_decode_partial(*d, g, q, k_thin, v_cache, seq_lens, kept_idx,
+                                                   keep, softmax_scale, (float*)ws, nullptr,
+                                                   (hipStream_t)stream));
+    if (st != THINK_OK) return st;
+    return hip_status(thinkkv::launch_decode_combine(*d, g, seq_lens, out, (const float*)ws,
+                                                     nullptr, (hipStream_t)stream));
+}
+
 int think_decode_attn_partial(const think_dims* d, const void* q, const void* k_thin,
                               const void* v_cache, const int32_t* seq_lens,
                               const int32_t* kept_idx, int32_t keep, float softmax_scale,

@@ -268,6 +268,10 @@ hipError_t launch_decode_partial(const think_dims& d, const DecodeGeom& g, const
                                  const void* k_thin, const void* v_cache, const int32_t* seq_lens,
                                  const int32_t* kept_idx, int keep, float scale, float* partials,
                                  int32_t* stash, hipStream_t s);
+// Bytes of the per-device scratch array of the allocation-free decode, and its
+// device address on the current device (looked up once per device).
+constexpr size_t kStaticScratchBytes = (size_t)8 << 20;
+hipError_t static_scratch(void** ptr);
 // app: NULL, or the fused append (its stash replaces seq_lens as the lengths)
 hipError_t launch_decode_combine(const think_dims& d, const DecodeGeom& g, const int32_t* seq_lens,
                                  void* out, const float* partials, const AppendArgs* app,
