@@ -400,6 +400,17 @@ hipError_t launch_decode_partial(const think_dims& d, const DecodeGeom& g, const
     return hipGetLastError();
 }
 
+hipError_t launch_decode(const think_dims& d, const DecodeGeom& g, const void* q,
+                         const void* k_thin, const void* v_cache, const int32_t* seq_lens,
+                         const int32_t* kept_idx, int keep, float scale, void* out,
+                         void* workspace, hipStream_t s) {
+    float* partials = static_cast<float*>(workspace);
+    hipError_t e = launch_decode_partial(d, g, q, k_thin, v_cache, seq_lens, kept_idx, keep,
+                                         scale, partials, nullptr, s);
+    if (e != hipSuccess) return e;
+    return launch_decode_combine(d, g, seq_lens, out, partials, nullptr, s);
+}
+
 hipError_t launch_decode_combine(const think_dims& d, const DecodeGeom& g, const int32_t* seq_lens,
                                  void* out, const float* partials, const AppendArgs* app,
                                  hipStream_t s) {

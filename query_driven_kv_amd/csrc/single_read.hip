@@ -32,7 +32,8 @@
 // for every launch (a generation word in the workspace that every launch
 // advances, so graph replays differ too, with the call's own counter below
 // it), so a workspace with any previous contents works.  Every flag has one
-// writer, which stores it after a release fence; waiters read it with an
+// writer, which stores it once the data it publishes (written through to
+// memory with device-scope stores) is complete; waiters read it with an
 // atomic add of zero, which the memory system performs on the current value
 // (a plain load kept returning a copy cached in this chiplet's L2), then take
 // one acquire fence.  (One arrival counter updated by every workgroup
@@ -61,13 +62,16 @@ constexpr int kQEarly = 4;          // window rows per thread loaded with the K 
 constexpr int kSrSubK = 16;         // k-slices (of 512 vectors) per compaction sub-tile: 128 KiB
 constexpr uint32_t kSrSpinLimit = 1u << 22;
 
-// Raise a flag once the whole workgroup's stores are done.
+// Raise a flag once the whole workgroup's stores are done.  The data a flag
+// publishes (tile partials, window-query sums) is stored with device-scope
+// stores, which write through to memory; each thread waits until its own
+// have completed, so no cache write-back is needed before the flag (a release
+// fence here wrote back the chiplet's L2 once per workgroup: 2 us per launch).
 __device__ __forceinline__ void signal_flag(unsigned long long* f, unsigned long long tag) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (threadIdx.x == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (threadIdx.x == 0)
         __hip_atomic_store(f, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
 }
 
 // Wait until flags[0..n) all hold the tag (thread i watches flags i, i+512,
@@ -211,7 +215,8 @@ __global__ __launch_bounds__(kSrThreads) void k_score_compact_resident(SrParams 
     for (int o = tid; o < R; o += kSrThreads) {
         double s = 0.0;
         for (int r = 0; r < nsub; ++r) s += red[r * R + o];
-        p.partials[(size_t)tw * R + o] = (float)s;
+        __hip_atomic_store(p.partials + (size_t)tw * R + o, (float)s, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
 
     // window-query sums of squares of this workgroup's units: each thread
@@ -244,7 +249,8 @@ __global__ __launch_bounds__(kSrThreads) void k_score_compact_resident(SrParams 
             if (uu >= nunits || uu >= (w + 1) * upw) continue;
             double t = 0.0;
             for (int r = 0; r < kQRowGroups; ++r) t += red[r * kQUnits * EPV + o];
-            p.q2[(size_t)uu * EPV + o % EPV] = t;     // [b][nqv][EPV] = [b][Hq][D]
+            __hip_atomic_store(p.q2 + (size_t)uu * EPV + o % EPV, t, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);     // [b][nqv][EPV] = [b][Hq][D]
         }
     }
 

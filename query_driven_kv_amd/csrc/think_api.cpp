@@ -235,12 +235,8 @@ int think_decode_attn(const think_dims* d, const void* q, const void* k_thin,
     int st = check_decode(d, q, k_thin, v_cache, seq_lens, kept_idx, true, out, true, keep,
                           workspace, workspace_bytes, &g);
     if (st != THINK_OK) return st;
-    st = hip_status(thinkkv::launch_decode_partial(*d, g, q, k_thin, v_cache, seq_lens, kept_idx,
-                                                   keep, softmax_scale, (float*)workspace,
-                                                   nullptr, (hipStream_t)stream));
-    if (st != THINK_OK) return st;
-    return hip_status(thinkkv::launch_decode_combine(*d, g, seq_lens, out, (const float*)workspace,
-                                                     nullptr, (hipStream_t)stream));
+    return hip_status(thinkkv::launch_decode(*d, g, q, k_thin, v_cache, seq_lens, kept_idx, keep,
+                                             softmax_scale, out, workspace, (hipStream_t)stream));
 }
 
 int think_decode_attn_static(const think_dims* d, const void* q, const void* k_thin,
@@ -259,12 +255,8 @@ int think_decode_attn_static(const think_dims* d, const void* q, const void* k_t
     void* ws = nullptr;
     st = hip_status(thinkkv::static_scratch(&ws));
     if (st != THINK_OK) return st;
-    st = hip_status(thinkkv::launch_decode_partial(*d, g, q, k_thin, v_cache, seq_lens, kept_idx,
-                                                   keep, softmax_scale, (float*)ws, nullptr,
-                                                   (hipStream_t)stream));
-    if (st != THINK_OK) return st;
-    return hip_status(thinkkv::launch_decode_combine(*d, g, seq_lens, out, (const float*)ws,
-                                                     nullptr, (hipStream_t)stream));
+    return hip_status(thinkkv::launch_decode(*d, g, q, k_thin, v_cache, seq_lens, kept_idx, keep,
+                                             softmax_scale, out, ws, (hipStream_t)stream));
 }
 
 int think_decode_attn_partial(const think_dims* d, const void* q, const void* k_thin,

@@ -268,6 +268,11 @@ hipError_t launch_decode_partial(const think_dims& d, const DecodeGeom& g, const
                                  const void* k_thin, const void* v_cache, const int32_t* seq_lens,
                                  const int32_t* kept_idx, int keep, float scale, float* partials,
                                  int32_t* stash, hipStream_t s);
+// The whole decode: the chunk pass, then the merge kernel into out.
+hipError_t launch_decode(const think_dims& d, const DecodeGeom& g, const void* q,
+                         const void* k_thin, const void* v_cache, const int32_t* seq_lens,
+                         const int32_t* kept_idx, int keep, float scale, void* out,
+                         void* workspace, hipStream_t s);
 // Bytes of the per-device scratch array of the allocation-free decode, and its
 // device address on the current device (looked up once per device).
 constexpr size_t kStaticScratchBytes = (size_t)8 << 20;
