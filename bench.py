@@ -376,6 +376,36 @@ def prefill_time(wl, torch, qdk, chunk=8192, reps=3):
     return float(np.mean(t_w[1:])), float(np.mean(t_s[1:])), float(np.mean(t_c[1:]))
 
 
+def probe_ceiling(torch, dev, read_bytes, write_bytes, launches=64):
+    """The single-launch ceiling for a path's byte counts: back-to-back launches
+    of think_probe_stream (one launch reads read_bytes and writes write_bytes
+    with nothing else to do), each on a different window of a scratch buffer
+    so that the reads come from HBM.  Returns microseconds per launch."""
+    from query_driven_kv_amd import _lib
+    P = ctypes.c_void_p
+    r = (read_bytes + 255) // 256 * 256
+    w = (write_bytes + 255) // 256 * 256
+    nwin = 4 if r < (256 << 20) else 2
+    src = torch.empty(max(r * nwin, 16), dtype=torch.uint8, device=dev)
+    dst = torch.empty(max(w * nwin, 16), dtype=torch.uint8, device=dev)
+    sp = P(torch.cuda.current_stream().cuda_stream)
+    fn = _lib.lib.think_probe_stream
+    args = [(P(src.data_ptr() + (k % nwin) * r), read_bytes, P(dst.data_ptr() + (k % nwin) * w),
+             write_bytes, sp) for k in range(nwin)]
+    for k in range(8):
+        _lib.check("think_probe_stream", fn(*args[k % nwin]))
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for k in range(launches):
+        fn(*args[k % nwin])
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / launches
+    del src, dst
+    return us
+
+
 def decode_source_hash():
     """Hash of the chunk-pass kernel's code (its source and the shared header;
     comments and whitespace dropped), so only a change to that code retires
@@ -595,6 +625,16 @@ def measure(cfg, args, torch, qdk, dev, steps, warmup, extras):
         part_us, n_part, part_pct = wl.decode_kernel_times(sp, torch)
         log(f"{cfg.name}: chunk-pass kernel: {part_us:.2f} us mean over {n_part} launches")
     achieved = bm["dec_call"] / (part_us * 1e-6) / 1e9 if n_part else None
+    # single-launch ceilings for the same byte counts (stream-probe launches)
+    e = 2 if cfg.dtype == "bf16" else 4
+    K = tok * cfg.n_kv_heads * cfg.head_dim * e
+    Kt = tok * cfg.n_kv_heads * cfg.keep * e
+    Qw = cfg.batch * cfg.obs_window * cfg.n_q_heads * cfg.head_dim * e
+    dec_ceil = probe_ceiling(torch, dev, bm["dec_call"], 0)
+    sc_read = (K if wl.single_read else 2 * K) + Qw
+    sc_ceil = probe_ceiling(torch, dev, sc_read, Kt)
+    log(f"{cfg.name}: single-launch ceilings: decode bytes {dec_ceil:.2f} us, score+compact "
+        f"bytes {sc_ceil:.2f} us")
     rec = {
         "ms_per_step": round(ms_per_step, 4),
         "GBps": round(value, 2),
@@ -632,6 +672,20 @@ def measure(cfg, args, torch, qdk, dev, steps, warmup, extras):
                                 f"least 64), after the timed steps")},
         "near_ties": near,
         "input_copies": wl.ncopies,
+        "ceiling": {
+            "probe": ("think_probe_stream: one launch that only reads (and writes) the path's "
+                      "bytes, 512 workgroups x 512 threads, back-to-back launches on rotating "
+                      "windows so reads come from HBM"),
+            "decode": {"read_bytes": bm["dec_call"], "us_per_launch": round(dec_ceil, 2),
+                       "GBps": round(bm["dec_call"] / (dec_ceil * 1e-6) / 1e9, 1),
+                       "call_frac_of_ceiling": round(dec_ceil / dec_call_us, 4),
+                       "chunk_pass_frac_of_ceiling":
+                           round(dec_ceil / part_us, 4) if n_part else None},
+            "score_compact": {"read_bytes": sc_read, "write_bytes": Kt,
+                              "us_per_launch": round(sc_ceil, 2),
+                              "GBps": round((sc_read + Kt) / (sc_ceil * 1e-6) / 1e9, 1),
+                              "frac_of_ceiling": round(sc_ceil / (sc_ms * 1e3 / cfg.layers), 4)},
+        },
     }
     if extras:
         app_us, app_bytes = append_time(cfg, torch, qdk, dev)
@@ -732,6 +786,7 @@ def main():
         "kv_tokens_per_s": rec["kv_tokens_per_s"],
         "paths": rec["paths"],
         "roofline": rec["roofline"],
+        "ceiling": rec["ceiling"],
         "near_ties": rec["near_ties"],
         "input_copies": rec["input_copies"],
     }

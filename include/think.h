@@ -334,6 +334,17 @@ THINK_API int think_score_select_k2(const think_dims *d, const void *k2_state,
                                     int32_t keep, float *scores, int32_t *kept_idx,
                                     int32_t *near_tie, void *stream);
 
+/*
+ * Calibration helper, not part of the method: one launch that reads
+ * read_bytes from src and writes write_bytes to dst (any values) as fast as
+ * the device allows, so that a benchmark can state the single-launch ceiling
+ * for a path's byte counts.  Device pointers, 16-byte aligned; a pointer may
+ * be NULL only when its byte count is 0.  THINK_ERR_UNSUPPORTED for counts of
+ * 1 TiB or more.
+ */
+THINK_API int think_probe_stream(const void *src, size_t read_bytes, void *dst,
+                                 size_t write_bytes, void *stream);
+
 /* Static description of a status code. */
 THINK_API const char *think_status_string(int status);
 /* The hipError_t of the last THINK_ERR_HIP on this thread (0 if none). */

@@ -24,7 +24,7 @@ EXPORTS = ("think_abi_version", "think_keep_from_ratio", "think_score_workspace_
            "think_prefill_write_kv",
            "think_score_select_k2", "think_score_select_compact",
            "think_score_compact_workspace_bytes", "think_score_compact_single_read",
-           "think_score_compact_status", "think_single_read_test_give_up",
+           "think_score_compact_status", "think_single_read_test_give_up", "think_probe_stream",
            "think_status_string", "think_last_hip_error")
 
 
@@ -88,6 +88,8 @@ def _load():
     l.think_score_compact_status.restype = ctypes.c_int
     l.think_single_read_test_give_up.argtypes = [ctypes.c_int]
     l.think_single_read_test_give_up.restype = ctypes.c_int
+    l.think_probe_stream.argtypes = [vp, sz, vp, sz, vp]
+    l.think_probe_stream.restype = ctypes.c_int
     l.think_status_string.argtypes = [ctypes.c_int]
     l.think_status_string.restype = ctypes.c_char_p
     l.think_last_hip_error.restype = ctypes.c_int

@@ -353,6 +353,17 @@ int think_score_select_k2(const think_dims* d, const void* k2_state, size_t k2_s
                                                (hipStream_t)stream));
 }
 
+int think_probe_stream(const void* src, size_t read_bytes, void* dst, size_t write_bytes,
+                       void* stream) {
+    if ((read_bytes && !src) || (write_bytes && !dst)) return THINK_ERR_NULL;
+    if ((src && !aligned16(src)) || (dst && !aligned16(dst))) return THINK_ERR_UNSUPPORTED;
+    if (read_bytes >= ((size_t)1 << 40) || write_bytes >= ((size_t)1 << 40))
+        return THINK_ERR_UNSUPPORTED;
+    if (!read_bytes && !write_bytes) return THINK_OK;
+    return hip_status(
+            thinkkv::launch_probe_stream(src, read_bytes, dst, write_bytes, (hipStream_t)stream));
+}
+
 const char* think_status_string(int status) {
     switch (status) {
         case THINK_OK: return "ok";

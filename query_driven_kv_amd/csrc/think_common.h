@@ -277,6 +277,8 @@ hipError_t launch_decode(const think_dims& d, const DecodeGeom& g, const void* q
 // device address on the current device (looked up once per device).
 constexpr size_t kStaticScratchBytes = (size_t)8 << 20;
 hipError_t static_scratch(void** ptr);
+hipError_t launch_probe_stream(const void* src, size_t read_bytes, void* dst, size_t write_bytes,
+                               hipStream_t s);
 // app: NULL, or the fused append (its stash replaces seq_lens as the lengths)
 hipError_t launch_decode_combine(const think_dims& d, const DecodeGeom& g, const int32_t* seq_lens,
                                  void* out, const float* partials, const AppendArgs* app,

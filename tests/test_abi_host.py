@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_header_declarations_are_all_exported(L):
     names = declared_functions()
-    assert len(names) == 24
+    assert len(names) == 25
     assert sorted(L.EXPORTS) == names
     so = ctypes.CDLL(L.LIB_PATH)
     for n in names:
@@ -280,6 +280,15 @@ def test_single_read_test_hook_is_per_thread(L):
     t.join()
     assert seen == [0]                                    # another thread: its own setting
     assert lib.think_single_read_test_give_up(0) == 1
+
+
+def test_probe_stream_validation(L):
+    lib = L.lib
+    assert lib.think_probe_stream(None, 16, None, 0, None) == -1
+    assert lib.think_probe_stream(FAKE, 16, None, 16, None) == -1
+    assert lib.think_probe_stream(ctypes.c_void_p(0x100008), 16, None, 0, None) == -5
+    assert lib.think_probe_stream(FAKE, 1 << 40, None, 0, None) == -5
+    assert lib.think_probe_stream(None, 0, None, 0, None) == 0       # nothing to do
 
 
 def test_status_strings(L):
