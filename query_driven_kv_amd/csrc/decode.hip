@@ -82,7 +82,33 @@ constexpr int kMaxG = 16;
 template <int DT>
 using LogitT = typename std::conditional<DT == THINK_F32, double, float>::type;
 
+// The general chunk pass (any dtype, any head_dim that is a multiple of 8 up
+// to 256, any keep, G <= 16): workgroup = (256-token chunk, kv head, b), the
+// chunk walked in tiles of kTT = 32 tokens.  Per tile:
+//  * the tile's thin key rows of this head (keep contiguous elements each, at
+//    the token stride Hkv*keep) are loaded with consecutive lanes on
+//    consecutive elements and stored to LDS as fp32 (row stride keep + 1, so
+//    the logit reads below hit different banks);
+//  * its value rows (D contiguous elements, 16-byte aligned) are loaded as
+//    4-element quads straight into registers; both loads of the next tile are
+//    issued while this tile computes;
+//  * logits: 8 threads per token, each summing every 8th kept channel for all
+//    G heads, the 8 partial sums added across lanes;
+//  * online softmax: one wave per head (lane = token);
+//  * values: thread (column quad cq, token group tg) accumulates the G output
+//    rows of its columns over its tokens, rescaled when the running maximum
+//    moves; the token groups are added in order at the end.
+// Loads are buffer loads bounded to the tile's valid rows, so padding rows
+// read as zero and their logits are masked.
+constexpr int kTT = 32;
+
 template <int DT>
+__device__ __forceinline__ float elem_f32(uint32_t x) {
+    if constexpr (DT == THINK_F32) return __uint_as_float(x);
+    else return bf16_to_f32(x & 0xffffu);
+}
+
+template <int DT, int VR, int KR, int GM>
 __global__ __launch_bounds__(kThreads) void k_decode_partial(
         const typename Elem<DT>::T* __restrict__ q, const typename Elem<DT>::T* __restrict__ k_thin,
         const typename Elem<DT>::T* __restrict__ v_cache, const int32_t* __restrict__ seq_lens,
@@ -90,6 +116,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_partial(
         float scale, int nsplit, int rec, float* __restrict__ partials,
         int32_t* __restrict__ stash) {
     using E = Elem<DT>;
+    using LT = LogitT<DT>;
+    constexpr int e = E::kBytes;
     const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
     const int len = clamp_len(seq_lens, b, s_cap);
     if (stash && split == 0 && kv == 0 && threadIdx.x == 0) stash[b] = len;   // fused append
@@ -97,13 +125,17 @@ __global__ __launch_bounds__(kThreads) void k_decode_partial(
     if (t0 >= len) return;                       // the combine stops before this chunk
     const int nt = min(kChunk, len - t0);
     const int Hq = Hkv * G;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-    using LT = LogitT<DT>;
-    __shared__ float qs[kMaxG * 256];            // gathered query, [g][j]
-    __shared__ LT p[kMaxG * kChunk];             // logits, then probabilities, [g][t]
-    __shared__ LT mrow[kMaxG];
-    __shared__ float lrow[kMaxG];
+    extern __shared__ __align__(16) unsigned char smem[];
+    LT* lg = reinterpret_cast<LT*>(smem);        // logits [kMaxG][kTT]
+    LT* ms = lg + kMaxG * kTT;                   // running maxima [kMaxG]
+    float* ls = reinterpret_cast<float*>(ms + kMaxG);   // running sums [kMaxG]
+    float* al = ls + kMaxG;                      // this tile's rescale factors [kMaxG]
+    float* pf = al + kMaxG;                      // probabilities [kMaxG][kTT]
+    float* qs = pf + kMaxG * kTT;                // gathered query [G][keep]
+    float* kt = qs + G * keep;                   // thin key rows [kTT][keep + 1], then a
+    const int ks = keep + 1;                     // reduction buffer [kThreads][4]
 
     for (int i = tid; i < G * keep; i += kThreads) {
         const int g = i / keep, j = i - g * keep;
@@ -111,62 +143,211 @@ __global__ __launch_bounds__(kThreads) void k_decode_partial(
         c = c < 0 ? 0 : (c >= D ? D - 1 : c);
         qs[i] = E::load(q, ((size_t)b * Hq + kv * G + g) * D + c);
     }
-    __syncthreads();
+    if (tid < kMaxG) {
+        ms[tid] = -INFINITY;
+        ls[tid] = 0.0f;
+    }
 
-    if (tid < nt) {
-        const size_t kr = (((size_t)b * s_cap + t0 + tid) * Hkv + kv) * keep;
-        LT acc[kMaxG];
+    // this thread's key elements of a tile: element f = tid + 256 i of the
+    // tile's kTT x keep block is (row f / keep, channel f % keep)
+    uint32_t rj[KR];
+    {
+        int r = tid / keep, j = tid - (tid / keep) * keep;
+        const int dr = kThreads / keep, dj = kThreads - dr * keep;
 #pragma unroll
-        for (int g = 0; g < kMaxG; ++g) acc[g] = 0;
-        for (int j = 0; j < keep; ++j) {
-            const LT x = E::load(k_thin, kr + j);
+        for (int i = 0; i < KR; ++i) {
+            rj[i] = ((uint32_t)r << 16) | (uint32_t)j;
+            j += dj;
+            r += dr;
+            if (j >= keep) {
+                j -= keep;
+                ++r;
+            }
+        }
+    }
+    const int rs = Hkv * keep;                   // thin-row stride (elements)
+    // value columns in quads; threads past TG * DQ (when DQ does not divide
+    // 256) hold no tokens.  VR * TG >= kTT (the launcher's choice of VR).
+    const int DQ = D >> 2, TG = kThreads / DQ;   // column quads, token groups
+    const int cq = tid % DQ, tg = tid < TG * DQ ? tid / DQ : kTT;
+    const size_t kbase = ((size_t)b * s_cap + t0) * rs + (size_t)kv * keep;
+    const size_t vbase = (((size_t)b * s_cap + t0) * Hkv + kv) * (size_t)D;
+    const int ntiles = (nt + kTT - 1) / kTT;
+
+    using VQ = typename std::conditional<DT == THINK_F32, uint4, uint2>::type;
+    uint32_t kr[KR];
+    VQ vq[VR], vn[VR];
+    // issue tile `tile`'s loads (an empty range past the last tile: zeros, no traffic)
+    auto load_tile = [&](int tile, uint32_t (&kd)[KR], VQ (&vd)[VR]) {
+        const int tb = tile * kTT;
+        const int ntt = tile < ntiles ? min(kTT, nt - tb) : 0;
+        const auto rk = make_rsrc(k_thin + kbase + (size_t)tb * rs,
+                                  ntt > 0 ? (uint32_t)(((ntt - 1) * rs + keep) * e) : 0u);
+        const auto rv = make_rsrc(v_cache + vbase + (size_t)tb * Hkv * D,
+                                  ntt > 0 ? (uint32_t)(((ntt - 1) * Hkv * D + D) * e) : 0u);
 #pragma unroll
-            for (int g = 0; g < kMaxG; ++g)
-                if (g < G) acc[g] = fma((LT)qs[g * keep + j], x, acc[g]);
+        for (int i = 0; i < KR; ++i) {
+            const int r = (int)(rj[i] >> 16), j = (int)(rj[i] & 0xffffu);
+            const uint32_t off = r < ntt ? (uint32_t)((r * rs + j) * e) : kOff;
+            if constexpr (DT == THINK_F32)
+                kd[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, (int)off, 0, kNonTemporal);
+            else
+                kd[i] = __builtin_amdgcn_raw_buffer_load_b16(rk, (int)off, 0, kNonTemporal);
         }
 #pragma unroll
-        for (int g = 0; g < kMaxG; ++g)
-            if (g < G) p[g * kChunk + tid] = acc[g] * (LT)scale;
-    }
-    __syncthreads();
-
-    if (tid < G) {
-        LT* pr = p + tid * kChunk;
-        LT m = pr[0];
-        for (int t = 1; t < nt; ++t) m = pr[t] > m ? pr[t] : m;
-        float l = 0.0f;
-        for (int t = 0; t < nt; ++t) {
-            const float e = expf((float)(pr[t] - m));
-            pr[t] = e;
-            l += e;
+        for (int i = 0; i < VR; ++i) {
+            const int r = tg + i * TG;               // >= kTT for threads without tokens
+            const uint32_t off = r < ntt ? (uint32_t)((r * Hkv * D + 4 * cq) * e) : kOff;
+            if constexpr (DT == THINK_F32) {
+                const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)off, 0,
+                                                                        kNonTemporal);
+                vd[i] = make_uint4(w.x, w.y, w.z, w.w);
+            } else {
+                const unsigned long long w =
+                        __builtin_bit_cast(unsigned long long,
+                                           __builtin_amdgcn_raw_buffer_load_b64(rv, (int)off, 0,
+                                                                                kNonTemporal));
+                vd[i] = make_uint2((uint32_t)w, (uint32_t)(w >> 32));
+            }
         }
-        mrow[tid] = m;
-        lrow[tid] = l;
-    }
-    __syncthreads();
+    };
+    load_tile(0, kr, vq);
 
-    for (int d = tid; d < D; d += kThreads) {
-        float o[kMaxG];
+    float o[GM][4];                              // GM >= G: 4 or 16
 #pragma unroll
-        for (int g = 0; g < kMaxG; ++g) o[g] = 0.0f;
-        for (int t = 0; t < nt; ++t) {
-            const float v = E::load(v_cache, (((size_t)b * s_cap + t0 + t) * Hkv + kv) * D + d);
+    for (int g = 0; g < GM; ++g) o[g][0] = o[g][1] = o[g][2] = o[g][3] = 0.0f;
+
+    for (int tile = 0; tile < ntiles; ++tile) {
+        const int ntt = min(kTT, nt - tile * kTT);
+        __syncthreads();                         // LDS of the previous tile is free
 #pragma unroll
-            for (int g = 0; g < kMaxG; ++g)
-                if (g < G) o[g] = fmaf((float)p[g * kChunk + t], v, o[g]);
+        for (int i = 0; i < KR; ++i) {
+            const int r = (int)(rj[i] >> 16), j = (int)(rj[i] & 0xffffu);
+            if (r < kTT) kt[r * ks + j] = elem_f32<DT>(kr[i]);
+        }
+        __syncthreads();
+        load_tile(tile + 1, kr, vn);             // in flight while this tile computes
+
+        // logits: token r = tid / 8, channels j = p, p + 8, ... (p = tid % 8)
+        {
+            const int r = tid >> 3, pp = tid & 7;
+            LT acc[GM];
+#pragma unroll
+            for (int g = 0; g < GM; ++g) acc[g] = 0;
+            for (int j = pp; j < keep; j += 8) {
+                const LT x = (LT)kt[r * ks + j];
+#pragma unroll
+                for (int g = 0; g < GM; ++g)
+                    if (g < G) acc[g] = fma((LT)qs[g * keep + j], x, acc[g]);
+            }
+#pragma unroll
+            for (int g = 0; g < GM; ++g) {
+                if (g < G) {
+                    LT a = acc[g];
+                    a += __shfl_xor(a, 1);
+                    a += __shfl_xor(a, 2);
+                    a += __shfl_xor(a, 4);
+                    if (pp == 0) lg[g * kTT + r] = a * (LT)scale;
+                }
+            }
+        }
+        __syncthreads();
+
+        // online softmax, one wave per head
+        for (int g = wave; g < G; g += kThreads / 64) {
+            const bool ok = lane < ntt;
+            const LT x = ok ? lg[g * kTT + lane] : (LT)-INFINITY;
+            LT mx = x;
+            for (int off = 32; off > 0; off >>= 1) {
+                const LT y = __shfl_xor(mx, off);
+                mx = y > mx ? y : mx;
+            }
+            const LT mo = ms[g];
+            const LT mn = mx > mo ? mx : mo;
+            const float a = mo == (LT)-INFINITY ? 0.0f : expf((float)(mo - mn));
+            const float pe = ok ? expf((float)(x - mn)) : 0.0f;
+            if (lane < kTT) pf[g * kTT + lane] = pe;
+            float sum = pe;
+            for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+            if (lane == 0) {
+                ms[g] = mn;
+                ls[g] = ls[g] * a + sum;
+                al[g] = a;
+            }
+        }
+        __syncthreads();
+
+        // values
+        float vf[VR][4];
+#pragma unroll
+        for (int i = 0; i < VR; ++i) {
+            if constexpr (DT == THINK_F32) {
+                vf[i][0] = __uint_as_float(vq[i].x);
+                vf[i][1] = __uint_as_float(vq[i].y);
+                vf[i][2] = __uint_as_float(vq[i].z);
+                vf[i][3] = __uint_as_float(vq[i].w);
+            } else {
+                vf[i][0] = bf16_lo(vq[i].x);
+                vf[i][1] = bf16_hi(vq[i].x);
+                vf[i][2] = bf16_lo(vq[i].y);
+                vf[i][3] = bf16_hi(vq[i].y);
+            }
         }
 #pragma unroll
-        for (int g = 0; g < kMaxG; ++g)
-            if (g < G)
-                partials[(((size_t)b * Hq + kv * G + g) * nsplit + split) * rec + 4 + d] = o[g];
+        for (int g = 0; g < GM; ++g) {
+            if (g < G) {
+                const float a = al[g];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) o[g][c] *= a;
+#pragma unroll
+                for (int i = 0; i < VR; ++i) {
+                    const int r = tg + i * TG;
+                    const float pv = r < kTT ? pf[g * kTT + r] : 0.0f;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) o[g][c] = fmaf(pv, vf[i][c], o[g][c]);
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < VR; ++i) vq[i] = vn[i];
     }
+
+    // records: (m, l, m - fp32(m)) and o, the token groups added in order
+    float* red = kt;
     if (tid < G) {
         float* r = partials + (((size_t)b * Hq + kv * G + tid) * nsplit + split) * rec;
-        const LT m = mrow[tid];
+        const LT m = ms[tid];
         r[0] = (float)m;
-        r[1] = lrow[tid];
+        r[1] = ls[tid];
         r[2] = (float)(m - (LT)(float)m);        // zero for bf16
     }
+#pragma unroll
+    for (int g = 0; g < GM; ++g) {
+        if (g < G) {
+            __syncthreads();
+#pragma unroll
+            for (int c = 0; c < 4; ++c) red[tid * 4 + c] = o[g][c];
+            __syncthreads();
+            if (tid < DQ) {
+                float s4[4] = {0.f, 0.f, 0.f, 0.f};
+                for (int t = 0; t < TG; ++t)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) s4[c] += red[(t * DQ + tid) * 4 + c];
+                float* r = partials + (((size_t)b * Hq + kv * G + g) * nsplit + split) * rec + 4;
+                *reinterpret_cast<float4*>(r + 4 * tid) = make_float4(s4[0], s4[1], s4[2], s4[3]);
+            }
+        }
+    }
+}
+
+// dynamic LDS of the general chunk pass
+size_t decode_partial_lds(const think_dims& d, int keep) {
+    const int G = d.n_q_heads / d.n_kv_heads;
+    const size_t lt = d.dtype == THINK_F32 ? 8 : 4;
+    const size_t kt = (size_t)kTT * (keep + 1) > (size_t)kThreads * 4 ? (size_t)kTT * (keep + 1)
+                                                                      : (size_t)kThreads * 4;
+    return (size_t)kMaxG * kTT * lt + kMaxG * lt + 2 * kMaxG * 4 + (size_t)kMaxG * kTT * 4 +
+           (size_t)G * keep * 4 + kt * 4;
 }
 
 // Merge the chunks of one (b, h).  The block is (D/4) x SG threads, each
@@ -387,17 +568,42 @@ hipError_t launch_decode_partial(const think_dims& d, const DecodeGeom& g, const
                                   partials, stash, s);
     const int G = d.n_q_heads / d.n_kv_heads;
     dim3 grid(g.nsplit, d.n_kv_heads, d.batch);
-    if (d.dtype == THINK_BF16)
-        k_decode_partial<THINK_BF16><<<grid, kThreads, 0, s>>>(
-            (const uint16_t*)q, (const uint16_t*)k_thin, (const uint16_t*)v_cache, seq_lens,
-            kept_idx, d.seq_capacity, d.n_kv_heads, G, d.head_dim, keep, scale, g.nsplit, g.rec,
-            partials, stash);
-    else
-        k_decode_partial<THINK_F32><<<grid, kThreads, 0, s>>>(
-            (const float*)q, (const float*)k_thin, (const float*)v_cache, seq_lens, kept_idx,
-            d.seq_capacity, d.n_kv_heads, G, d.head_dim, keep, scale, g.nsplit, g.rec, partials,
-            stash);
-    return hipGetLastError();
+    const size_t lds = decode_partial_lds(d, keep);
+    // value rows per thread and tile: kTT tokens over 256 / (D / 4) token
+    // groups, rounded up to a power of two
+    const int tgs = kThreads / (d.head_dim / 4), need = (kTT + tgs - 1) / tgs;
+    const int vr = need > 4 ? 8 : need > 2 ? 4 : need > 1 ? 2 : 1;
+    const bool wide = keep > 64;                 // key elements per thread and tile: 8 or 32
+    auto go = [&](auto dt, auto vrc, auto krc) {
+        constexpr int DT = decltype(dt)::value, VR = decltype(vrc)::value,
+                      KR = decltype(krc)::value;
+        using T = typename Elem<DT>::T;
+        if (G <= 4)
+            k_decode_partial<DT, VR, KR, 4><<<grid, kThreads, lds, s>>>(
+                    (const T*)q, (const T*)k_thin, (const T*)v_cache, seq_lens, kept_idx,
+                    d.seq_capacity, d.n_kv_heads, G, d.head_dim, keep, scale, g.nsplit, g.rec,
+                    partials, stash);
+        else
+            k_decode_partial<DT, VR, KR, kMaxG><<<grid, kThreads, lds, s>>>(
+                    (const T*)q, (const T*)k_thin, (const T*)v_cache, seq_lens, kept_idx,
+                    d.seq_capacity, d.n_kv_heads, G, d.head_dim, keep, scale, g.nsplit, g.rec,
+                    partials, stash);
+        return hipGetLastError();
+    };
+    auto by_k = [&](auto dt, auto vrc) {
+        return wide ? go(dt, vrc, std::integral_constant<int, 32>{})
+                    : go(dt, vrc, std::integral_constant<int, 8>{});
+    };
+    auto by_v = [&](auto dt) {
+        switch (vr) {
+            case 8: return by_k(dt, std::integral_constant<int, 8>{});
+            case 4: return by_k(dt, std::integral_constant<int, 4>{});
+            case 2: return by_k(dt, std::integral_constant<int, 2>{});
+            default: return by_k(dt, std::integral_constant<int, 1>{});
+        }
+    };
+    return d.dtype == THINK_BF16 ? by_v(std::integral_constant<int, THINK_BF16>{})
+                                 : by_v(std::integral_constant<int, THINK_F32>{});
 }
 
 hipError_t launch_decode(const think_dims& d, const DecodeGeom& g, const void* q,
