@@ -17,7 +17,8 @@ OUT = os.path.join(PKG, "libthinkkv.so")
 OBJDIR = os.path.join(PKG, "_build")
 
 SOURCES = ["think_api.cpp", "score.hip", "select.hip", "compact.hip", "decode.hip",
-           "decode_mfma.hip", "append.hip", "prefill.hip", "single_read.hip", "probe.hip"]
+           "decode_general_f32.hip", "decode_general_bf16.hip", "decode_mfma.hip", "append.hip",
+           "prefill.hip", "single_read.hip", "probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-fvisibility=hidden",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

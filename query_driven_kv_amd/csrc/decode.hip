@@ -14,14 +14,16 @@
 // (running max m, sum l, unnormalised o[D]) to the workspace; a combine
 // kernel merges the chunks of each (b, h) in ascending chunk order.
 //
-// This file holds the general kernel (any dtype, any keep, G <= 16) and the
-// combine kernel.  The bf16 matrix-core kernel for the bandwidth-critical
-// shapes is in decode_mfma.hip and writes the same partial records.
+// This file holds the geometry, the dispatch and the combine kernel.  The
+// chunk passes are the bf16 matrix-core kernel for the bandwidth-critical
+// shapes (decode_mfma.hip) and the general kernel (any dtype, any keep,
+// G <= 16; decode_general_impl.h, built per dtype); both write the same
+// partial records.
 #include <atomic>
 #include <mutex>
 #include <type_traits>
 
-#include "think_common.h"
+#include "decode_general.h"
 
 namespace thinkkv {
 
@@ -70,284 +72,10 @@ hipError_t launch_decode_mfma(const think_dims& d, const DecodeGeom& g, const vo
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kChunk = 256;    // tokens per workgroup (general kernel)
-constexpr int kMaxG = 16;
-
-// Logits and running maxima of fp32 inputs are kept in fp64: with fp32 inputs
-// of large magnitude (a logit of a few hundred has an fp32 ulp of 3e-5) an
-// fp32 logit alone would spend the fp32 accuracy bound on its rounding.  The
-// record's maximum is stored as its fp32 rounding plus the fp32 residual (in
-// the record's third word).  bf16 inputs keep fp32 throughout.
-template <int DT>
-using LogitT = typename std::conditional<DT == THINK_F32, double, float>::type;
-
-// The general chunk pass (any dtype, any head_dim that is a multiple of 8 up
-// to 256, any keep, G <= 16): workgroup = (256-token chunk, kv head, b), the
-// chunk walked in tiles of kTT = 32 tokens.  Per tile:
-//  * the tile's thin key rows of this head (keep contiguous elements each, at
-//    the token stride Hkv*keep) are loaded with consecutive lanes on
-//    consecutive elements and stored to LDS as fp32 (row stride keep + 1, so
-//    the logit reads below hit different banks);
-//  * its value rows (D contiguous elements, 16-byte aligned) are loaded as
-//    4-element quads straight into registers; both loads of the next tile are
-//    issued while this tile computes;
-//  * logits: 8 threads per token, each summing every 8th kept channel for all
-//    G heads, the 8 partial sums added across lanes;
-//  * online softmax: one wave per head (lane = token);
-//  * values: thread (column quad cq, token group tg) accumulates the G output
-//    rows of its columns over its tokens, rescaled when the running maximum
-//    moves; the token groups are added in order at the end.
-// Loads are buffer loads bounded to the tile's valid rows, so padding rows
-// read as zero and their logits are masked.
-constexpr int kTT = 32;
-
-template <int DT>
-__device__ __forceinline__ float elem_f32(uint32_t x) {
-    if constexpr (DT == THINK_F32) return __uint_as_float(x);
-    else return bf16_to_f32(x & 0xffffu);
-}
-
-template <int DT, int VR, int KR, int GM>
-__global__ __launch_bounds__(kThreads) void k_decode_partial(
-        const typename Elem<DT>::T* __restrict__ q, const typename Elem<DT>::T* __restrict__ k_thin,
-        const typename Elem<DT>::T* __restrict__ v_cache, const int32_t* __restrict__ seq_lens,
-        const int32_t* __restrict__ kept_idx, int s_cap, int Hkv, int G, int D, int keep,
-        float scale, int nsplit, int rec, float* __restrict__ partials,
-        int32_t* __restrict__ stash) {
-    using E = Elem<DT>;
-    using LT = LogitT<DT>;
-    constexpr int e = E::kBytes;
-    const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
-    const int len = clamp_len(seq_lens, b, s_cap);
-    if (stash && split == 0 && kv == 0 && threadIdx.x == 0) stash[b] = len;   // fused append
-    const int t0 = split * kChunk;
-    if (t0 >= len) return;                       // the combine stops before this chunk
-    const int nt = min(kChunk, len - t0);
-    const int Hq = Hkv * G;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-    extern __shared__ __align__(16) unsigned char smem[];
-    LT* lg = reinterpret_cast<LT*>(smem);        // logits [kMaxG][kTT]
-    LT* ms = lg + kMaxG * kTT;                   // running maxima [kMaxG]
-    float* ls = reinterpret_cast<float*>(ms + kMaxG);   // running sums [kMaxG]
-    float* al = ls + kMaxG;                      // this tile's rescale factors [kMaxG]
-    float* pf = al + kMaxG;                      // probabilities [kMaxG][kTT]
-    float* qs = pf + kMaxG * kTT;                // gathered query [G][keep]
-    float* kt = qs + G * keep;                   // thin key rows [kTT][keep + 1], then a
-    const int ks = keep + 1;                     // reduction buffer [kThreads][4]
-
-    for (int i = tid; i < G * keep; i += kThreads) {
-        const int g = i / keep, j = i - g * keep;
-        int c = kept_idx[((size_t)b * Hkv + kv) * keep + j];
-        c = c < 0 ? 0 : (c >= D ? D - 1 : c);
-        qs[i] = E::load(q, ((size_t)b * Hq + kv * G + g) * D + c);
-    }
-    if (tid < kMaxG) {
-        ms[tid] = -INFINITY;
-        ls[tid] = 0.0f;
-    }
-
-    // this thread's key elements of a tile: element f = tid + 256 i of the
-    // tile's kTT x keep block is (row f / keep, channel f % keep)
-    uint32_t rj[KR];
-    {
-        int r = tid / keep, j = tid - (tid / keep) * keep;
-        const int dr = kThreads / keep, dj = kThreads - dr * keep;
-#pragma unroll
-        for (int i = 0; i < KR; ++i) {
-            rj[i] = ((uint32_t)r << 16) | (uint32_t)j;
-            j += dj;
-            r += dr;
-            if (j >= keep) {
-                j -= keep;
-                ++r;
-            }
-        }
-    }
-    const int rs = Hkv * keep;                   // thin-row stride (elements)
-    // value columns in quads; threads past TG * DQ (when DQ does not divide
-    // 256) hold no tokens.  VR * TG >= kTT (the launcher's choice of VR).
-    const int DQ = D >> 2, TG = kThreads / DQ;   // column quads, token groups
-    const int cq = tid % DQ, tg = tid < TG * DQ ? tid / DQ : kTT;
-    const size_t kbase = ((size_t)b * s_cap + t0) * rs + (size_t)kv * keep;
-    const size_t vbase = (((size_t)b * s_cap + t0) * Hkv + kv) * (size_t)D;
-    const int ntiles = (nt + kTT - 1) / kTT;
-
-    using VQ = typename std::conditional<DT == THINK_F32, uint4, uint2>::type;
-    uint32_t kr[KR];
-    VQ vq[VR], vn[VR];
-    // issue tile `tile`'s loads (an empty range past the last tile: zeros, no traffic)
-    auto load_tile = [&](int tile, uint32_t (&kd)[KR], VQ (&vd)[VR]) {
-        const int tb = tile * kTT;
-        const int ntt = tile < ntiles ? min(kTT, nt - tb) : 0;
-        const auto rk = make_rsrc(k_thin + kbase + (size_t)tb * rs,
-                                  ntt > 0 ? (uint32_t)(((ntt - 1) * rs + keep) * e) : 0u);
-        const auto rv = make_rsrc(v_cache + vbase + (size_t)tb * Hkv * D,
-                                  ntt > 0 ? (uint32_t)(((ntt - 1) * Hkv * D + D) * e) : 0u);
-#pragma unroll
-        for (int i = 0; i < KR; ++i) {
-            const int r = (int)(rj[i] >> 16), j = (int)(rj[i] & 0xffffu);
-            const uint32_t off = r < ntt ? (uint32_t)((r * rs + j) * e) : kOff;
-            if constexpr (DT == THINK_F32)
-                kd[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, (int)off, 0, kNonTemporal);
-            else
-                kd[i] = __builtin_amdgcn_raw_buffer_load_b16(rk, (int)off, 0, kNonTemporal);
-        }
-#pragma unroll
-        for (int i = 0; i < VR; ++i) {
-            const int r = tg + i * TG;               // >= kTT for threads without tokens
-            const uint32_t off = r < ntt ? (uint32_t)((r * Hkv * D + 4 * cq) * e) : kOff;
-            if constexpr (DT == THINK_F32) {
-                const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)off, 0,
-                                                                        kNonTemporal);
-                vd[i] = make_uint4(w.x, w.y, w.z, w.w);
-            } else {
-                const unsigned long long w =
-                        __builtin_bit_cast(unsigned long long,
-                                           __builtin_amdgcn_raw_buffer_load_b64(rv, (int)off, 0,
-                                                                                kNonTemporal));
-                vd[i] = make_uint2((uint32_t)w, (uint32_t)(w >> 32));
-            }
-        }
-    };
-    load_tile(0, kr, vq);
-
-    float o[GM][4];                              // GM >= G: 4 or 16
-#pragma unroll
-    for (int g = 0; g < GM; ++g) o[g][0] = o[g][1] = o[g][2] = o[g][3] = 0.0f;
-
-    for (int tile = 0; tile < ntiles; ++tile) {
-        const int ntt = min(kTT, nt - tile * kTT);
-        __syncthreads();                         // LDS of the previous tile is free
-#pragma unroll
-        for (int i = 0; i < KR; ++i) {
-            const int r = (int)(rj[i] >> 16), j = (int)(rj[i] & 0xffffu);
-            if (r < kTT) kt[r * ks + j] = elem_f32<DT>(kr[i]);
-        }
-        __syncthreads();
-        load_tile(tile + 1, kr, vn);             // in flight while this tile computes
-
-        // logits: token r = tid / 8, channels j = p, p + 8, ... (p = tid % 8)
-        {
-            const int r = tid >> 3, pp = tid & 7;
-            LT acc[GM];
-#pragma unroll
-            for (int g = 0; g < GM; ++g) acc[g] = 0;
-            for (int j = pp; j < keep; j += 8) {
-                const LT x = (LT)kt[r * ks + j];
-#pragma unroll
-                for (int g = 0; g < GM; ++g)
-                    if (g < G) acc[g] = fma((LT)qs[g * keep + j], x, acc[g]);
-            }
-#pragma unroll
-            for (int g = 0; g < GM; ++g) {
-                if (g < G) {
-                    LT a = acc[g];
-                    a += __shfl_xor(a, 1);
-                    a += __shfl_xor(a, 2);
-                    a += __shfl_xor(a, 4);
-                    if (pp == 0) lg[g * kTT + r] = a * (LT)scale;
-                }
-            }
-        }
-        __syncthreads();
-
-        // online softmax, one wave per head
-        for (int g = wave; g < G; g += kThreads / 64) {
-            const bool ok = lane < ntt;
-            const LT x = ok ? lg[g * kTT + lane] : (LT)-INFINITY;
-            LT mx = x;
-            for (int off = 32; off > 0; off >>= 1) {
-                const LT y = __shfl_xor(mx, off);
-                mx = y > mx ? y : mx;
-            }
-            const LT mo = ms[g];
-            const LT mn = mx > mo ? mx : mo;
-            const float a = mo == (LT)-INFINITY ? 0.0f : expf((float)(mo - mn));
-            const float pe = ok ? expf((float)(x - mn)) : 0.0f;
-            if (lane < kTT) pf[g * kTT + lane] = pe;
-            float sum = pe;
-            for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
-            if (lane == 0) {
-                ms[g] = mn;
-                ls[g] = ls[g] * a + sum;
-                al[g] = a;
-            }
-        }
-        __syncthreads();
-
-        // values
-        float vf[VR][4];
-#pragma unroll
-        for (int i = 0; i < VR; ++i) {
-            if constexpr (DT == THINK_F32) {
-                vf[i][0] = __uint_as_float(vq[i].x);
-                vf[i][1] = __uint_as_float(vq[i].y);
-                vf[i][2] = __uint_as_float(vq[i].z);
-                vf[i][3] = __uint_as_float(vq[i].w);
-            } else {
-                vf[i][0] = bf16_lo(vq[i].x);
-                vf[i][1] = bf16_hi(vq[i].x);
-                vf[i][2] = bf16_lo(vq[i].y);
-                vf[i][3] = bf16_hi(vq[i].y);
-            }
-        }
-#pragma unroll
-        for (int g = 0; g < GM; ++g) {
-            if (g < G) {
-                const float a = al[g];
-#pragma unroll
-                for (int c = 0; c < 4; ++c) o[g][c] *= a;
-#pragma unroll
-                for (int i = 0; i < VR; ++i) {
-                    const int r = tg + i * TG;
-                    const float pv = r < kTT ? pf[g * kTT + r] : 0.0f;
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) o[g][c] = fmaf(pv, vf[i][c], o[g][c]);
-                }
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < VR; ++i) vq[i] = vn[i];
-    }
-
-    // records: (m, l, m - fp32(m)) and o, the token groups added in order
-    float* red = kt;
-    if (tid < G) {
-        float* r = partials + (((size_t)b * Hq + kv * G + tid) * nsplit + split) * rec;
-        const LT m = ms[tid];
-        r[0] = (float)m;
-        r[1] = ls[tid];
-        r[2] = (float)(m - (LT)(float)m);        // zero for bf16
-    }
-#pragma unroll
-    for (int g = 0; g < GM; ++g) {
-        if (g < G) {
-            __syncthreads();
-#pragma unroll
-            for (int c = 0; c < 4; ++c) red[tid * 4 + c] = o[g][c];
-            __syncthreads();
-            if (tid < DQ) {
-                float s4[4] = {0.f, 0.f, 0.f, 0.f};
-                for (int t = 0; t < TG; ++t)
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) s4[c] += red[(t * DQ + tid) * 4 + c];
-                float* r = partials + (((size_t)b * Hq + kv * G + g) * nsplit + split) * rec + 4;
-                *reinterpret_cast<float4*>(r + 4 * tid) = make_float4(s4[0], s4[1], s4[2], s4[3]);
-            }
-        }
-    }
-}
-
-// dynamic LDS of the general chunk pass
-size_t decode_partial_lds(const think_dims& d, int keep) {
-    const int G = d.n_q_heads / d.n_kv_heads;
-    const size_t lt = d.dtype == THINK_F32 ? 8 : 4;
-    const size_t kt = (size_t)kTT * (keep + 1) > (size_t)kThreads * 4 ? (size_t)kTT * (keep + 1)
-                                                                      : (size_t)kThreads * 4;
-    return (size_t)kMaxG * kTT * lt + kMaxG * lt + 2 * kMaxG * 4 + (size_t)kMaxG * kTT * 4 +
-           (size_t)G * keep * 4 + kt * 4;
+int pow2_at_least(int n) {
+    int p = 1;
+    while (p < n) p <<= 1;
+    return p;
 }
 
 // Merge the chunks of one (b, h).  The block is (D/4) x SG threads, each
@@ -547,11 +275,55 @@ __global__ __launch_bounds__(1024) void k_decode_combine(
 
 }  // namespace
 
+// Tile shape of the general chunk pass.  Value quads and key units per thread
+// cover the tile (powers of two); 64-token tiles when the tile's loads take at
+// most 24 registers a thread with 16-byte key units (small rows: fewer tiles,
+// so less per-tile work per byte).  kp: keep rounded up to whole 4-channel
+// chunks for each of the 256 / TT logit lanes; ks: the key tile's LDS row
+// stride, kp or kp + 4 * LP so that it is an odd number of lane-group spans
+// and the 16-byte logit reads of neighbouring rows fall in different banks.
+GeneralTile general_tile(const think_dims& d, int keep) {
+    GeneralTile t{};
+    const int e = d.dtype == THINK_F32 ? 4 : 2;
+    const int D = d.head_dim;
+    t.kb = keep * e % 16 == 0 ? 16 : e;
+    t.gm = d.n_q_heads / d.n_kv_heads <= 4 ? 4 : kGenMaxG;
+    auto vr_for = [&](int tt) {
+        const int tgs = kGenThreads / (D / 4);
+        return pow2_at_least((tt + tgs - 1) / tgs);
+    };
+    auto kr_for = [&](int tt) {
+        const int units = tt * (keep * e / t.kb);
+        const int k = pow2_at_least((units + kGenThreads - 1) / kGenThreads);
+        return t.kb == 16 ? k : (k < 8 ? 8 : k);
+    };
+    t.tt = 32;
+    if (t.kb == 16) {
+        const int vr = vr_for(64), kr = kr_for(64);
+        if (vr <= 4 && kr <= 2 && kr * 4 + vr * (e == 4 ? 4 : 2) <= 24) t.tt = 64;
+    }
+    t.vr = vr_for(t.tt);
+    t.kr = kr_for(t.tt);
+    const int span = 4 * (kGenThreads / t.tt);
+    t.kp = (keep + span - 1) / span * span;
+    t.ks = (t.kp / span) % 2 == 1 ? t.kp : t.kp + span;
+    return t;
+}
+
+size_t general_lds_bytes(const think_dims& d, int keep, const GeneralTile& t) {
+    const int G = d.n_q_heads / d.n_kv_heads;
+    const size_t lt = d.dtype == THINK_F32 ? 8 : 4;
+    const size_t kt = (size_t)t.tt * t.ks > (size_t)kGenThreads * 4 ? (size_t)t.tt * t.ks
+                                                                   : (size_t)kGenThreads * 4;
+    return (size_t)kGenMaxG * t.tt * lt + kGenMaxG * lt + 2 * kGenMaxG * 4 +
+           (size_t)kGenMaxG * t.tt * 4 + (size_t)G * t.kp * 4 + kt * 4;
+}
+
 DecodeGeom decode_geom(const think_dims& d, int keep) {
     DecodeGeom g{};
     g.mfma = mfma_decode_supported(d, keep);
     g.mode = !g.mfma ? kFixedChunk : (d.batch >= 2 && d.batch <= 64 ? kBalanced : kSeqChunk);
-    g.chunk = g.mfma ? mfma_decode_chunk(d, keep) : kChunk;
+    g.chunk = g.mfma ? mfma_decode_chunk(d, keep) : kGenChunk;
     g.nsplit = (d.seq_capacity + g.chunk - 1) / g.chunk;
     g.rec = d.head_dim + 4;
     g.stash_offset = (size_t)d.batch * d.n_q_heads * g.nsplit * g.rec * sizeof(float);
@@ -566,44 +338,11 @@ hipError_t launch_decode_partial(const think_dims& d, const DecodeGeom& g, const
     if (g.mfma)
         return launch_decode_mfma(d, g, q, k_thin, v_cache, seq_lens, kept_idx, keep, scale,
                                   partials, stash, s);
-    const int G = d.n_q_heads / d.n_kv_heads;
-    dim3 grid(g.nsplit, d.n_kv_heads, d.batch);
-    const size_t lds = decode_partial_lds(d, keep);
-    // value rows per thread and tile: kTT tokens over 256 / (D / 4) token
-    // groups, rounded up to a power of two
-    const int tgs = kThreads / (d.head_dim / 4), need = (kTT + tgs - 1) / tgs;
-    const int vr = need > 4 ? 8 : need > 2 ? 4 : need > 1 ? 2 : 1;
-    const bool wide = keep > 64;                 // key elements per thread and tile: 8 or 32
-    auto go = [&](auto dt, auto vrc, auto krc) {
-        constexpr int DT = decltype(dt)::value, VR = decltype(vrc)::value,
-                      KR = decltype(krc)::value;
-        using T = typename Elem<DT>::T;
-        if (G <= 4)
-            k_decode_partial<DT, VR, KR, 4><<<grid, kThreads, lds, s>>>(
-                    (const T*)q, (const T*)k_thin, (const T*)v_cache, seq_lens, kept_idx,
-                    d.seq_capacity, d.n_kv_heads, G, d.head_dim, keep, scale, g.nsplit, g.rec,
-                    partials, stash);
-        else
-            k_decode_partial<DT, VR, KR, kMaxG><<<grid, kThreads, lds, s>>>(
-                    (const T*)q, (const T*)k_thin, (const T*)v_cache, seq_lens, kept_idx,
-                    d.seq_capacity, d.n_kv_heads, G, d.head_dim, keep, scale, g.nsplit, g.rec,
-                    partials, stash);
-        return hipGetLastError();
-    };
-    auto by_k = [&](auto dt, auto vrc) {
-        return wide ? go(dt, vrc, std::integral_constant<int, 32>{})
-                    : go(dt, vrc, std::integral_constant<int, 8>{});
-    };
-    auto by_v = [&](auto dt) {
-        switch (vr) {
-            case 8: return by_k(dt, std::integral_constant<int, 8>{});
-            case 4: return by_k(dt, std::integral_constant<int, 4>{});
-            case 2: return by_k(dt, std::integral_constant<int, 2>{});
-            default: return by_k(dt, std::integral_constant<int, 1>{});
-        }
-    };
-    return d.dtype == THINK_BF16 ? by_v(std::integral_constant<int, THINK_BF16>{})
-                                 : by_v(std::integral_constant<int, THINK_F32>{});
+    if (d.dtype == THINK_BF16)
+        return launch_decode_general_bf16(d, g.nsplit, g.rec, q, k_thin, v_cache, seq_lens,
+                                          kept_idx, keep, scale, partials, stash, s);
+    return launch_decode_general_f32(d, g.nsplit, g.rec, q, k_thin, v_cache, seq_lens, kept_idx,
+                                     keep, scale, partials, stash, s);
 }
 
 hipError_t launch_decode(const think_dims& d, const DecodeGeom& g, const void* q,
