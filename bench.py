@@ -63,6 +63,11 @@ def parse():
                     help="skip the append, append+decode and prefill figures")
     ap.add_argument("--parity", action="store_true",
                     help="with --no-cpu-baseline: still check layer 0 against the oracle")
+    ap.add_argument("--decode-shape", action="append", default=[],
+                    metavar="DTYPE,B,HQ,HKV,D,S,KEEP",
+                    help="instead of the workload: time the decode alone (chunk pass + "
+                         "combine) on this synthetic shape at full length, one JSON line per "
+                         "shape; repeatable")
     return ap.parse_args()
 
 
@@ -406,6 +411,80 @@ def probe_ceiling(torch, dev, read_bytes, write_bytes, launches=64):
     return us
 
 
+def decode_shape_bench(spec, torch, dev, calls=200):
+    """Decode alone on one synthetic shape "dtype,B,Hq,Hkv,D,S,keep" with every
+    sequence at full length: mean time per think_decode_attn call (chunk pass
+    + combine, back to back), the chunk pass's mean launch duration (events
+    around each launch in split-phase form), algorithmic GB/s and the
+    single-launch ceiling for the call's bytes.  Inputs are N(0, 1) drawn on
+    the device, in enough copies (rotated call to call) that the reads come
+    from HBM."""
+    from query_driven_kv_amd import _lib
+    lib, P = _lib.lib, ctypes.c_void_p
+    f = spec.split(",")
+    dt = f[0]
+    B, Hq, Hkv, D, S, keep = (int(x) for x in f[1:])
+    if dt not in ("f32", "bf16"):
+        raise SystemExit(f"--decode-shape: dtype must be f32 or bf16, got {dt!r}")
+    tdt, code, e = (torch.float32, 0, 4) if dt == "f32" else (torch.bfloat16, 1, 2)
+    per_copy = B * S * Hkv * (keep + D) * e
+    ncopies = max(2, min(8, -(-(640 << 20) // per_copy)))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20260721)
+    kt = [torch.randn(B, S, Hkv, keep, generator=gen, device=dev).to(tdt) for _ in range(ncopies)]
+    v = [torch.randn(B, S, Hkv, D, generator=gen, device=dev).to(tdt) for _ in range(ncopies)]
+    q = torch.randn(B, Hq, D, generator=gen, device=dev).to(tdt)
+    idx = torch.sort(torch.rand(B * Hkv, D, generator=gen, device=dev).argsort(dim=1)[:, :keep],
+                     dim=1)[0].to(torch.int32).reshape(B, Hkv, keep).contiguous()
+    lens = torch.full((B,), S, dtype=torch.int32, device=dev)
+    out = torch.empty(B, Hq, D, dtype=tdt, device=dev)
+    dims = _lib.think_dims(B, Hq, Hkv, D, S, code)
+    d = ctypes.byref(dims)
+    wsn = lib.think_decode_workspace_bytes(d, keep)
+    ws = torch.empty(wsn, dtype=torch.uint8, device=dev)
+    sp = P(torch.cuda.current_stream().cuda_stream)
+    scale = ctypes.c_float(1.0 / float(np.sqrt(D)))
+    args = [(P(q.data_ptr()), P(kt[c].data_ptr()), P(v[c].data_ptr()), P(lens.data_ptr()),
+             P(idx.data_ptr())) for c in range(ncopies)]
+
+    def call(k):
+        _lib.check("think_decode_attn", lib.think_decode_attn(
+            d, *args[k % ncopies], keep, scale, P(out.data_ptr()), P(ws.data_ptr()), wsn, sp))
+
+    for k in range(8):
+        call(k)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for k in range(calls):
+        call(k)
+    e1.record()
+    torch.cuda.synchronize()
+    us_call = e0.elapsed_time(e1) * 1e3 / calls
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(64)]
+    for k, (a, b) in enumerate(ev):
+        a.record()
+        _lib.check("think_decode_attn_partial", lib.think_decode_attn_partial(
+            d, *args[k % ncopies], keep, scale, P(ws.data_ptr()), wsn, sp))
+        b.record()
+        _lib.check("think_decode_attn_combine", lib.think_decode_attn_combine(
+            d, P(lens.data_ptr()), keep, P(out.data_ptr()), P(ws.data_ptr()), wsn, sp))
+    torch.cuda.synchronize()
+    us_chunk = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    rd = B * S * Hkv * (keep + D) * e + B * Hq * D * e
+    wr = B * Hq * D * e
+    del kt, v
+    torch.cuda.empty_cache()
+    ceil_us = probe_ceiling(torch, dev, rd, wr)
+    return {"decode_shape": {"dtype": dt, "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv,
+                             "head_dim": D, "seq_len": S, "keep": keep},
+            "us_per_call": round(us_call, 2), "chunk_pass_us": round(us_chunk, 2),
+            "bytes_per_call": rd + wr, "GBps": round((rd + wr) / us_call / 1e3, 1),
+            "ceiling_us": round(ceil_us, 2), "frac_of_ceiling": round(ceil_us / us_call, 3),
+            "calls": calls, "input_copies": ncopies}
+
+
 def decode_source_hash():
     """Hash of the chunk-pass kernel's code (its source and the shared header;
     comments and whitespace dropped), so only a change to that code retires
@@ -739,6 +818,11 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.decode_shape:
+        for spec in args.decode_shape:
+            log(f"decode shape {spec}")
+            print(json.dumps(decode_shape_bench(spec, torch, dev)), flush=True)
+        return
     cfg = kvsynth.CONFIGS[args.workload]
     if args.decode_steps > 0:
         import dataclasses

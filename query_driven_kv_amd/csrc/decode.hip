@@ -362,9 +362,17 @@ hipError_t launch_decode_combine(const think_dims& d, const DecodeGeom& g, const
     AppendArgs ap{};
     if (app) ap = *app;
     dim3 cgrid(d.n_q_heads, d.batch);
+    // sub-groups: at least min(16, 1024 / D), and enough that each merges at
+    // most 8 chunk slots (one batch of record loads in flight), within 1024
+    // threads
+    const int d4 = d.head_dim / 4;
     int sg_count = 1024 / d.head_dim;
     if (sg_count > 16) sg_count = 16;
-    const int cthreads = d.head_dim / 4 * sg_count;
+    const int sg_slots = (g.nsplit + 7) / 8;
+    if (sg_count < sg_slots) sg_count = sg_slots;
+    if (sg_count > 1024 / d4) sg_count = 1024 / d4;
+    if (sg_count > 64) sg_count = 64;
+    const int cthreads = d4 * sg_count;
     if (d.dtype == THINK_BF16)
         k_decode_combine<THINK_BF16><<<cgrid, cthreads, 0, s>>>(
             partials, seq_lens, d.seq_capacity, g.chunk, g.mode, g.nsplit, g.rec, d.head_dim,

@@ -1,4 +1,4 @@
-// decode_mfma.hip - bf16 matrix-core kernel for stage (d), head_dim 128.
+// decode_mfma.hip - bf16 matrix-core kernel for stage (d), head_dim 128 or 64.
 //
 // "ThinK: Thinner Key Cache by Query-Driven Pruning", Method details ->
 // Technical framework, last step: attention runs on the thinner key cache
@@ -26,7 +26,10 @@
 //               8 tokens per lane), rounded to bf16 - no data movement;
 //           B = V: lane (l%16 = d octet, l/16 = token quad) loads the 16-byte
 //               V rows of its 8 tokens; 8 output tiles, tile c taking element c
-//               of each row, re-paired per token with 16-bit permutes.
+//               of each row, re-paired per token with 16-bit permutes.  At
+//               head_dim 64 the lanes of octets 8..15 read zeros and their
+//               output columns are dropped (the same instruction stream moves
+//               half the value bytes).
 // The token order inside one 32-token step is a permutation shared by A and
 // B of the value product, so no transposition through LDS is needed.
 //
@@ -53,7 +56,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kD = 128;
+constexpr int kQS = 128;      // LDS row stride of the gathered query (keep <= 128)
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 
@@ -126,7 +129,7 @@ struct LaneOffsets {
 // loaded if it starts before the row's last kept channel ends (it then lies
 // inside the descriptor's range, which is rounded up to 16 bytes); for
 // KAL = 8 that is exactly "the octet holds kept channels".
-template <int KB>
+template <int KB, int D>
 __device__ __forceinline__ LaneOffsets<KB> lane_offsets(int keep, size_t kt_row, size_t v_row,
                                                         int n16, int q4, uint32_t delta) {
     LaneOffsets<KB> lo;
@@ -152,7 +155,8 @@ __device__ __forceinline__ LaneOffsets<KB> lane_offsets(int keep, size_t kt_row,
             lo.kt[h][e] = need ? al + 16u * k : kOff;
         }
     }
-    lo.v0 = (uint32_t)((4 * q4 * v_row + 8 * n16) * 2);
+    // head_dim 64: lanes n16 >= 8 hold no column octet and read zeros
+    lo.v0 = 8 * n16 < D ? (uint32_t)((4 * q4 * v_row + 8 * n16) * 2) : kOff;
     return lo;
 }
 
@@ -301,7 +305,7 @@ __device__ __forceinline__ void compute_step(const Frag<KB, KAL>& f, const LaneO
     O[7] = mfma(pa, v_column<7>(f.v), O[7]);
 }
 
-template <int KB, int KAL, bool SL>
+template <int KB, int KAL, bool SL, int D>
 __global__ __launch_bounds__(kThreads, (KAL == 8 && KB <= 2) ? 3 : 2) void k_decode_mfma(
         const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_thin,
         const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ seq_lens,
@@ -334,8 +338,8 @@ __global__ __launch_bounds__(kThreads, (KAL == 8 && KB <= 2) ? 3 : 2) void k_dec
     const int lane = tid & 63, wave = tid >> 6;
     const int n16 = lane & 15, q4 = lane >> 4;
 
-    __shared__ __align__(16) uint16_t s_q[16 * kD];            // gathered query [g][j]
-    __shared__ float s_o[kWaves * 16 * kD];      // per-wave O [w][g][d]
+    __shared__ __align__(16) uint16_t s_q[16 * kQS];           // gathered query [g][j]
+    __shared__ float s_o[kWaves * 16 * D];       // per-wave O [w][g][d]
     __shared__ float s_m[kWaves * 16], s_l[kWaves * 16];
 
     // Prologue, ordered so the stream starts after one memory round trip:
@@ -400,14 +404,14 @@ __global__ __launch_bounds__(kThreads, (KAL == 8 && KB <= 2) ? 3 : 2) void k_dec
         t0 = split * cb;
     }
     const auto rsrc_q =
-            make_rsrc(q + ((size_t)b * Hq + (size_t)kv * G) * kD, (uint32_t)(G * kD * 2));
+            make_rsrc(q + ((size_t)b * Hq + (size_t)kv * G) * D, (uint32_t)(G * D * 2));
     uint16_t qv[kGather];
 #pragma unroll
     for (int r = 0; r < kGather; ++r) {
         const int i = tid + r * kThreads;
         const int g = i / (KB * 32), j = i - g * (KB * 32);
-        const int c = cidx[r] < 0 ? 0 : (cidx[r] >= kD ? kD - 1 : cidx[r]);
-        const int off = j < keep ? (g * kD + c) * 2 : (int)kOff;
+        const int c = cidx[r] < 0 ? 0 : (cidx[r] >= D ? D - 1 : cidx[r]);
+        const int off = j < keep ? (g * D + c) * 2 : (int)kOff;
         qv[r] = __builtin_amdgcn_raw_buffer_load_b16(rsrc_q, off, 0, 0);
     }
 
@@ -415,7 +419,7 @@ __global__ __launch_bounds__(kThreads, (KAL == 8 && KB <= 2) ? 3 : 2) void k_dec
     const int ws = t0 + __builtin_amdgcn_readfirstlane(wave) * tw;   // wave-uniform
     const int we = min(ws + tw, len);
     const size_t kt_row = (size_t)Hkv * keep;
-    const size_t v_row = (size_t)Hkv * kD;
+    const size_t v_row = (size_t)Hkv * D;
     // this wave's first rows of kv head kv; the valid bytes of a step starting
     // at token ts end at the last valid token's row.  Steps advance by 32 rows
     // of 2*Hkv*keep bytes, a multiple of 64, so the row's offset from a 16-byte
@@ -424,9 +428,9 @@ __global__ __launch_bounds__(kThreads, (KAL == 8 && KB <= 2) ? 3 : 2) void k_dec
     // aligned, so the bytes read below the row and past the range's end stay
     // within the 16-byte blocks of valid rows; for KAL = 8 delta is 0).
     const uint16_t* kw = k_thin + ((size_t)b * s_cap + ws) * kt_row + (size_t)kv * keep;
-    const uint16_t* vw = v_cache + ((size_t)b * s_cap + ws) * v_row + (size_t)kv * kD;
+    const uint16_t* vw = v_cache + ((size_t)b * s_cap + ws) * v_row + (size_t)kv * D;
     const uint32_t delta = (uint32_t)(reinterpret_cast<uintptr_t>(kw) & 15u);
-    const LaneOffsets<KB> lo = lane_offsets<KB>(keep, kt_row, v_row, n16, q4, delta);
+    const LaneOffsets<KB> lo = lane_offsets<KB, D>(keep, kt_row, v_row, n16, q4, delta);
     uint32_t vs[8];                              // V rows of tokens (i & 3) + 16 * (i >> 2)
 #pragma unroll
     for (int i = 0; i < 8; ++i) vs[i] = (uint32_t)(((i & 3) + 16 * (i >> 2)) * v_row * 2);
@@ -445,7 +449,7 @@ __global__ __launch_bounds__(kThreads, (KAL == 8 && KB <= 2) ? 3 : 2) void k_dec
     };
     auto rsrc_v = [&](int ts) {
         const int nt = min(32, we - ts);
-        const uint32_t bytes = nt > 0 ? (uint32_t)(((nt - 1) * v_row + kD) * 2) : 0u;
+        const uint32_t bytes = nt > 0 ? (uint32_t)(((nt - 1) * v_row + D) * 2) : 0u;
         return make_rsrc(vw + (size_t)(ts - ws) * v_row, bytes);
     };
 
@@ -461,13 +465,13 @@ __global__ __launch_bounds__(kThreads, (KAL == 8 && KB <= 2) ? 3 : 2) void k_dec
     for (int r = 0; r < kGather; ++r) {
         const int i = tid + r * kThreads;
         const int g = i / (KB * 32), j = i - g * (KB * 32);
-        s_q[g * kD + j] = qv[r];
+        s_q[g * kQS + j] = qv[r];
     }
     __syncthreads();
     uint4 qB[KB];                                // B operand: lane holds qS[jb*32+8*q4+i][g=n16]
 #pragma unroll
     for (int jb = 0; jb < KB; ++jb)
-        qB[jb] = *reinterpret_cast<const uint4*>(&s_q[n16 * kD + jb * 32 + 8 * q4]);
+        qB[jb] = *reinterpret_cast<const uint4*>(&s_q[n16 * kQS + jb * 32 + 8 * q4]);
 
     f32x4 O[8];
 #pragma unroll
@@ -492,11 +496,11 @@ __global__ __launch_bounds__(kThreads, (KAL == 8 && KB <= 2) ? 3 : 2) void k_dec
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int g = 4 * q4 + i;
-            if (g < G) s_o[(wave * 16 + g) * kD + 8 * n16 + c] = O[c][i];
+            if (g < G && 8 * n16 < D) s_o[(wave * 16 + g) * D + 8 * n16 + c] = O[c][i];
         }
     __syncthreads();
-    for (int e = tid; e < G * kD; e += kThreads) {
-        const int g = e / kD, d = e - g * kD;
+    for (int e = tid; e < G * D; e += kThreads) {
+        const int g = e / D, d = e - g * D;
         float M = s_m[g];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w * 16 + g]);
@@ -505,7 +509,7 @@ __global__ __launch_bounds__(kThreads, (KAL == 8 && KB <= 2) ? 3 : 2) void k_dec
         for (int w = 0; w < kWaves; ++w) {
             const float f = expf(s_m[w * 16 + g] - M);
             L = fmaf(f, s_l[w * 16 + g], L);
-            o = fmaf(f, s_o[(w * 16 + g) * kD + d], o);
+            o = fmaf(f, s_o[(w * 16 + g) * D + d], o);
         }
         float* r = partials + (mode == kBalanced
                                        ? ((size_t)(kv * G + g) * nsplit * nb + slot) * rec
@@ -519,7 +523,7 @@ __global__ __launch_bounds__(kThreads, (KAL == 8 && KB <= 2) ? 3 : 2) void k_dec
 
 }
 
-template <int KB>
+template <int KB, int D>
 hipError_t launch_kb(int kal, dim3 grid, hipStream_t s, const uint16_t* q, const uint16_t* kt,
                      const uint16_t* v, const int32_t* lens, const int32_t* idx, int s_cap,
                      int Hkv, int G, int keep, float scale, int chunk, int nsplit, int rec,
@@ -528,15 +532,15 @@ hipError_t launch_kb(int kal, dim3 grid, hipStream_t s, const uint16_t* q, const
     // their neighbours (keep 51 at 128K tokens: 81 -> 68 us per call)
     const bool shared_lines = (keep * 2) % 128 != 0;
     if (kal == 8 && !shared_lines)
-        k_decode_mfma<KB, 8, false><<<grid, kThreads, 0, s>>>(
+        k_decode_mfma<KB, 8, false, D><<<grid, kThreads, 0, s>>>(
                 q, kt, v, lens, idx, s_cap, Hkv, G, keep, scale, chunk, nsplit, rec, mode, part,
                 stash);
     else if (kal == 8)
-        k_decode_mfma<KB, 8, true><<<grid, kThreads, 0, s>>>(
+        k_decode_mfma<KB, 8, true, D><<<grid, kThreads, 0, s>>>(
                 q, kt, v, lens, idx, s_cap, Hkv, G, keep, scale, chunk, nsplit, rec, mode, part,
                 stash);
     else
-        k_decode_mfma<KB, 0, true><<<grid, kThreads, 0, s>>>(
+        k_decode_mfma<KB, 0, true, D><<<grid, kThreads, 0, s>>>(
                 q, kt, v, lens, idx, s_cap, Hkv, G, keep, scale, chunk, nsplit, rec, mode, part,
                 stash);
     return hipGetLastError();
@@ -545,8 +549,8 @@ hipError_t launch_kb(int kal, dim3 grid, hipStream_t s, const uint16_t* q, const
 }  // namespace
 
 bool mfma_decode_supported(const think_dims& d, int keep) {
-    return d.dtype == THINK_BF16 && d.head_dim == kD && d.n_q_heads / d.n_kv_heads <= 16 &&
-           keep >= 1 && keep <= kD;
+    return d.dtype == THINK_BF16 && (d.head_dim == 128 || d.head_dim == 64) &&
+           d.n_q_heads / d.n_kv_heads <= 16 && keep >= 1 && keep <= d.head_dim;
 }
 
 // Tokens per workgroup: a multiple of 128 (one 32-token step per wave), sized
@@ -580,16 +584,22 @@ hipError_t launch_decode_mfma(const think_dims& d, const DecodeGeom& g, const vo
     auto qp = (const uint16_t*)q;
     auto kp = (const uint16_t*)k_thin;
     auto vp = (const uint16_t*)v_cache;
-    auto go = [&](auto kb) {
-        return launch_kb<decltype(kb)::value>(kal, grid, s, qp, kp, vp, seq_lens, kept_idx,
-                                              d.seq_capacity, d.n_kv_heads, G, keep, scale,
-                                              g.chunk, g.nsplit, g.rec, g.mode, partials, stash);
+    auto go = [&](auto kb, auto dc) {
+        return launch_kb<decltype(kb)::value, decltype(dc)::value>(
+                kal, grid, s, qp, kp, vp, seq_lens, kept_idx, d.seq_capacity, d.n_kv_heads, G,
+                keep, scale, g.chunk, g.nsplit, g.rec, g.mode, partials, stash);
     };
+    if (d.head_dim == 64) {                      // keep <= 64: one or two channel blocks
+        using D64 = std::integral_constant<int, 64>;
+        return KB == 1 ? go(std::integral_constant<int, 1>{}, D64{})
+                       : go(std::integral_constant<int, 2>{}, D64{});
+    }
+    using D128 = std::integral_constant<int, 128>;
     switch (KB) {
-        case 1: return go(std::integral_constant<int, 1>{});
-        case 2: return go(std::integral_constant<int, 2>{});
-        case 3: return go(std::integral_constant<int, 3>{});
-        default: return go(std::integral_constant<int, 4>{});
+        case 1: return go(std::integral_constant<int, 1>{}, D128{});
+        case 2: return go(std::integral_constant<int, 2>{}, D128{});
+        case 3: return go(std::integral_constant<int, 3>{}, D128{});
+        default: return go(std::integral_constant<int, 4>{}, D128{});
     }
 }
 
