@@ -41,6 +41,7 @@ namespace {
 constexpr int kMaxDevices = 256;
 std::atomic<void*> g_scratch_ptr[kMaxDevices];
 std::mutex g_scratch_mu;
+std::atomic<int> g_cu_count[kMaxDevices];   // compute units per device, 0 until asked
 }  // namespace
 
 hipError_t static_scratch(void** ptr) {
@@ -319,11 +320,45 @@ size_t general_lds_bytes(const think_dims& d, int keep, const GeneralTile& t) {
            (size_t)kGenMaxG * t.tt * 4 + (size_t)G * t.kp * 4 + kt * 4;
 }
 
+// 256 tokens a workgroup, halved (down to 64) while the halved chunk's
+// workgroups all fit on the GPU at once (the instance's workgroups per compute
+// unit times the compute units): a call that fills less than one wave of
+// resident workgroups leaves per-tile latency uncovered, one that spills into
+// a second wave pays a tail (bf16 D 256, 4 kv heads, 32K tokens: 512 -> 1024
+// workgroups at four a unit, 46.3 -> 42.0 us; fp32 D 128, 32 kv heads, 4K
+// tokens, three a unit: stays at 512, 38.1 us at 1024 against 32.4).  Without a
+// device to ask (a size query on a host with no GPU) the chunk stays 256.
+int general_chunk(const think_dims& d, int keep) {
+    const int per_cu = d.dtype == THINK_BF16 ? general_blocks_per_cu_bf16(d, keep)
+                                             : general_blocks_per_cu_f32(d, keep);
+    int dev = 0;
+    if (per_cu <= 0 || hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return kGenChunk;
+    }
+    int cus = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (cus <= 0) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0) {
+            (void)hipGetLastError();
+            return kGenChunk;
+        }
+        g_cu_count[dev].store(cus, std::memory_order_relaxed);
+    }
+    const int64_t resident = (int64_t)per_cu * cus;
+    auto wgs = [&](int c) {
+        return (int64_t)((d.seq_capacity + c - 1) / c) * d.n_kv_heads * d.batch;
+    };
+    int chunk = kGenChunk;
+    while (chunk > 64 && wgs(chunk / 2) <= resident) chunk /= 2;
+    return chunk;
+}
+
 DecodeGeom decode_geom(const think_dims& d, int keep) {
     DecodeGeom g{};
     g.mfma = mfma_decode_supported(d, keep);
     g.mode = !g.mfma ? kFixedChunk : (d.batch >= 2 && d.batch <= 64 ? kBalanced : kSeqChunk);
-    g.chunk = g.mfma ? mfma_decode_chunk(d, keep) : kGenChunk;
+    g.chunk = g.mfma ? mfma_decode_chunk(d, keep) : general_chunk(d, keep);
     g.nsplit = (d.seq_capacity + g.chunk - 1) / g.chunk;
     g.rec = d.head_dim + 4;
     g.stash_offset = (size_t)d.batch * d.n_q_heads * g.nsplit * g.rec * sizeof(float);
@@ -339,10 +374,10 @@ hipError_t launch_decode_partial(const think_dims& d, const DecodeGeom& g, const
         return launch_decode_mfma(d, g, q, k_thin, v_cache, seq_lens, kept_idx, keep, scale,
                                   partials, stash, s);
     if (d.dtype == THINK_BF16)
-        return launch_decode_general_bf16(d, g.nsplit, g.rec, q, k_thin, v_cache, seq_lens,
-                                          kept_idx, keep, scale, partials, stash, s);
-    return launch_decode_general_f32(d, g.nsplit, g.rec, q, k_thin, v_cache, seq_lens, kept_idx,
-                                     keep, scale, partials, stash, s);
+        return launch_decode_general_bf16(d, g.chunk, g.nsplit, g.rec, q, k_thin, v_cache,
+                                          seq_lens, kept_idx, keep, scale, partials, stash, s);
+    return launch_decode_general_f32(d, g.chunk, g.nsplit, g.rec, q, k_thin, v_cache, seq_lens,
+                                     kept_idx, keep, scale, partials, stash, s);
 }
 
 hipError_t launch_decode(const think_dims& d, const DecodeGeom& g, const void* q,

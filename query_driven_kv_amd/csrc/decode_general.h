@@ -16,7 +16,8 @@
 namespace thinkkv {
 
 constexpr int kGenThreads = 256;   // threads per workgroup
-constexpr int kGenChunk = 256;     // tokens per workgroup (one chunk slot)
+constexpr int kGenChunk = 256;     // tokens per workgroup (one chunk slot), halved down to 64
+                                   // while a call has fewer than 1024 workgroups
 constexpr int kGenMaxG = 16;       // query heads per kv head
 
 // Logits and running maxima of fp32 inputs are kept in fp64: with fp32 inputs
@@ -41,14 +42,23 @@ struct GeneralTile {
 GeneralTile general_tile(const think_dims& d, int keep);
 size_t general_lds_bytes(const think_dims& d, int keep, const GeneralTile& t);
 
-// One launch of the general chunk pass (grid nsplit x Hkv x B, 256 threads),
-// writing the same partial records as the matrix-core kernel.
-hipError_t launch_decode_general_f32(const think_dims& d, int nsplit, int rec, const void* q,
-                                     const void* k_thin, const void* v_cache,
+// Tokens per chunk of the general pass for a call of these dims and keep.
+int general_chunk(const think_dims& d, int keep);
+
+// Workgroups of the call's general-pass instance one compute unit holds at
+// once, 0 if the runtime cannot say (no device).
+int general_blocks_per_cu_f32(const think_dims& d, int keep);
+int general_blocks_per_cu_bf16(const think_dims& d, int keep);
+
+// One launch of the general chunk pass (grid nsplit x Hkv x B, 256 threads,
+// `chunk` tokens a workgroup), writing the same partial records as the
+// matrix-core kernel.
+hipError_t launch_decode_general_f32(const think_dims& d, int chunk, int nsplit, int rec,
+                                     const void* q, const void* k_thin, const void* v_cache,
                                      const int32_t* seq_lens, const int32_t* kept_idx, int keep,
                                      float scale, float* partials, int32_t* stash, hipStream_t s);
-hipError_t launch_decode_general_bf16(const think_dims& d, int nsplit, int rec, const void* q,
-                                      const void* k_thin, const void* v_cache,
+hipError_t launch_decode_general_bf16(const think_dims& d, int chunk, int nsplit, int rec,
+                                      const void* q, const void* k_thin, const void* v_cache,
                                       const int32_t* seq_lens, const int32_t* kept_idx, int keep,
                                       float scale, float* partials, int32_t* stash, hipStream_t s);
 

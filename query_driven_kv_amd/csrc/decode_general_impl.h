@@ -3,7 +3,7 @@
 // decode_general_f32.hip and decode_general_bf16.hip, which build one dtype
 // each.
 //
-// Workgroup = (256-token chunk, kv head, b), 256 threads; the G query heads of
+// Workgroup = (token chunk of 64..256, kv head, b), 256 threads; the G query heads of
 // the group share every byte of K_thin and V it streams.  The chunk is walked
 // in tiles of TT = 32 or 64 tokens, NB tiles in a ring of register buffers:
 // while tile t computes, the loads of tiles t+1 .. t+NB-1 are in flight.
@@ -33,6 +33,7 @@
 // writes one partial record (m, l, m - fp32(m), pad, o[D]) per query head.
 #pragma once
 
+#include <mutex>
 #include <type_traits>
 
 #include "decode_general.h"
@@ -111,7 +112,7 @@ __global__ __launch_bounds__(kGenThreads) void k_decode_general(
         const typename Elem<DT>::T* __restrict__ q, const typename Elem<DT>::T* __restrict__ k_thin,
         const typename Elem<DT>::T* __restrict__ v_cache, const int32_t* __restrict__ seq_lens,
         const int32_t* __restrict__ kept_idx, int s_cap, int Hkv, int G, int D, int keep, int kp,
-        int ks, float scale, int nsplit, int rec, float* __restrict__ partials,
+        int ks, float scale, int chunk, int nsplit, int rec, float* __restrict__ partials,
         int32_t* __restrict__ stash) {
     using LT = LogitT<DT>;
     constexpr int e = Elem<DT>::kBytes;
@@ -131,9 +132,9 @@ __global__ __launch_bounds__(kGenThreads) void k_decode_general(
                                                           0, 0);
     const int len = clamp_len(seq_lens, b, s_cap);
     if (stash && split == 0 && kv == 0 && tid == 0) stash[b] = len;   // fused append
-    const int t0 = split * kGenChunk;
+    const int t0 = split * chunk;
     if (t0 >= len) return;                       // the combine stops before this chunk
-    const int nt = min(kGenChunk, len - t0);
+    const int nt = min(chunk, len - t0);
 
     extern __shared__ __align__(16) unsigned char smem[];
     LT* lg = reinterpret_cast<LT*>(smem);        // logits [kGenMaxG][TT]
@@ -412,34 +413,25 @@ __global__ __launch_bounds__(kGenThreads) void k_decode_general(
 
 }  // namespace
 
-// Launch for one dtype.  Only the (TT, VR, KR) combinations that keep <=
-// head_dim <= 256 can reach are built: 32-token tiles take 16-byte key units
-// numbering ceil(keep * e / 128) a thread, at most VR (fp32) or VR / 2 (bf16),
-// or one-element units numbering ceil(keep / 8), at most 4 * VR (8 when VR <=
+template <int DT>
+using GeneralKernel = void (*)(const typename Elem<DT>::T*, const typename Elem<DT>::T*,
+                               const typename Elem<DT>::T*, const int32_t*, const int32_t*, int,
+                               int, int, int, int, int, int, float, int, int, int, float*,
+                               int32_t*);
+
+// The instance for a tile shape (nullptr for a shape no instance covers).
+// Only the (TT, VR, KR) combinations that keep <= head_dim <= 256 can reach
+// are built: 32-token tiles take 16-byte key units numbering
+// ceil(keep * e / 128) a thread, at most VR (fp32) or VR / 2 (bf16), or
+// one-element units numbering ceil(keep / 8), at most 4 * VR (8 when VR <=
 // 2); 64-token tiles are chosen only with 16-byte units, VR <= 4 and KR <= 2.
 template <int DT>
-hipError_t launch_general(const think_dims& d, int nsplit, int rec, const void* q,
-                          const void* k_thin, const void* v_cache, const int32_t* seq_lens,
-                          const int32_t* kept_idx, int keep, float scale, float* partials,
-                          int32_t* stash, hipStream_t s) {
-    using T = typename Elem<DT>::T;
-    const int G = d.n_q_heads / d.n_kv_heads;
-    const GeneralTile t = general_tile(d, keep);
-    const size_t lds = general_lds_bytes(d, keep, t);
-    dim3 grid(nsplit, d.n_kv_heads, d.batch);
-    auto go = [&](auto ttc, auto vrc, auto kbc, auto krc) {
+GeneralKernel<DT> general_kernel(const GeneralTile& t) {
+    auto pick = [&](auto ttc, auto vrc, auto kbc, auto krc) -> GeneralKernel<DT> {
         constexpr int TT = decltype(ttc)::value, VR = decltype(vrc)::value,
                       KB = decltype(kbc)::value, KR = decltype(krc)::value;
-        auto run = [&](auto gmc) {
-            k_decode_general<DT, TT, VR, KB, KR, decltype(gmc)::value>
-                    <<<grid, kGenThreads, lds, s>>>(
-                            (const T*)q, (const T*)k_thin, (const T*)v_cache, seq_lens, kept_idx,
-                            d.seq_capacity, d.n_kv_heads, G, d.head_dim, keep, t.kp, t.ks, scale,
-                            nsplit, rec, partials, stash);
-            return hipGetLastError();
-        };
-        return t.gm == 4 ? run(std::integral_constant<int, 4>{})
-                         : run(std::integral_constant<int, kGenMaxG>{});
+        if (t.gm == 4) return k_decode_general<DT, TT, VR, KB, KR, 4>;
+        return k_decode_general<DT, TT, VR, KB, KR, kGenMaxG>;
     };
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
@@ -449,32 +441,32 @@ hipError_t launch_general(const think_dims& d, int nsplit, int rec, const void* 
     using I32 = std::integral_constant<int, 32>;
     using I64 = std::integral_constant<int, 64>;
     using KE = std::integral_constant<int, Elem<DT>::kBytes>;
-    auto tile32 = [&](auto vrc) {
+    auto tile32 = [&](auto vrc) -> GeneralKernel<DT> {
         constexpr int VR = decltype(vrc)::value;
         constexpr int kmax16 = DT == THINK_F32 ? VR : (VR > 1 ? VR / 2 : 1);
         constexpr int kmax1 = VR > 2 ? 4 * VR : 8;
         if (t.kb == 16) {
-            if (t.kr > kmax16) return hipErrorInvalidValue;
-            if constexpr (kmax16 >= 8) if (t.kr == 8) return go(I32{}, vrc, I16{}, I8{});
-            if constexpr (kmax16 >= 4) if (t.kr == 4) return go(I32{}, vrc, I16{}, I4{});
-            if constexpr (kmax16 >= 2) if (t.kr == 2) return go(I32{}, vrc, I16{}, I2{});
-            return go(I32{}, vrc, I16{}, I1{});
+            if (t.kr > kmax16) return nullptr;
+            if constexpr (kmax16 >= 8) if (t.kr == 8) return pick(I32{}, vrc, I16{}, I8{});
+            if constexpr (kmax16 >= 4) if (t.kr == 4) return pick(I32{}, vrc, I16{}, I4{});
+            if constexpr (kmax16 >= 2) if (t.kr == 2) return pick(I32{}, vrc, I16{}, I2{});
+            return pick(I32{}, vrc, I16{}, I1{});
         }
-        if (t.kr > kmax1) return hipErrorInvalidValue;
-        if constexpr (kmax1 >= 32) if (t.kr == 32) return go(I32{}, vrc, KE{}, I32{});
-        if constexpr (kmax1 >= 16) if (t.kr == 16) return go(I32{}, vrc, KE{}, I16{});
-        return go(I32{}, vrc, KE{}, I8{});
+        if (t.kr > kmax1) return nullptr;
+        if constexpr (kmax1 >= 32) if (t.kr == 32) return pick(I32{}, vrc, KE{}, I32{});
+        if constexpr (kmax1 >= 16) if (t.kr == 16) return pick(I32{}, vrc, KE{}, I16{});
+        return pick(I32{}, vrc, KE{}, I8{});
     };
-    auto tile64 = [&](auto vrc) {
-        if (t.kb != 16 || t.kr > 2) return hipErrorInvalidValue;
-        return t.kr == 2 ? go(I64{}, vrc, I16{}, I2{}) : go(I64{}, vrc, I16{}, I1{});
+    auto tile64 = [&](auto vrc) -> GeneralKernel<DT> {
+        if (t.kb != 16 || t.kr > 2) return nullptr;
+        return t.kr == 2 ? pick(I64{}, vrc, I16{}, I2{}) : pick(I64{}, vrc, I16{}, I1{});
     };
     if (t.tt == 64) {
         switch (t.vr) {
             case 4: return tile64(I4{});
             case 2: return tile64(I2{});
             case 1: return tile64(I1{});
-            default: return hipErrorInvalidValue;
+            default: return nullptr;
         }
     }
     switch (t.vr) {
@@ -483,6 +475,58 @@ hipError_t launch_general(const think_dims& d, int nsplit, int rec, const void* 
         case 2: return tile32(I2{});
         default: return tile32(I1{});
     }
+}
+
+// Workgroups of the call's instance that one compute unit holds at once
+// (registers and LDS), or 0 when it cannot be asked (no device).  Answers are
+// kept per (instance, LDS bytes, device) so a call asks the runtime once.
+template <int DT>
+int general_blocks_per_cu(const think_dims& d, int keep) {
+    const GeneralTile t = general_tile(d, keep);
+    const GeneralKernel<DT> fn = general_kernel<DT>(t);
+    const size_t lds = general_lds_bytes(d, keep, t);
+    int dev = 0;
+    if (!fn || hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();                 // leave no error behind for the next call
+        return 0;
+    }
+    struct Entry {
+        const void* fn;
+        size_t lds;
+        int dev, n;
+    };
+    static std::mutex mu;
+    static Entry cache[128];
+    static int used = 0;
+    std::lock_guard<std::mutex> lk(mu);
+    for (int i = 0; i < used; ++i)
+        if (cache[i].fn == reinterpret_cast<const void*>(fn) && cache[i].lds == lds &&
+            cache[i].dev == dev)
+            return cache[i].n;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(fn),
+                                                     kGenThreads, lds) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    if (used < 128) cache[used++] = Entry{reinterpret_cast<const void*>(fn), lds, dev, n};
+    return n;
+}
+
+template <int DT>
+hipError_t launch_general(const think_dims& d, int chunk, int nsplit, int rec, const void* q,
+                          const void* k_thin, const void* v_cache, const int32_t* seq_lens,
+                          const int32_t* kept_idx, int keep, float scale, float* partials,
+                          int32_t* stash, hipStream_t s) {
+    using T = typename Elem<DT>::T;
+    const GeneralTile t = general_tile(d, keep);
+    const GeneralKernel<DT> fn = general_kernel<DT>(t);
+    if (!fn) return hipErrorInvalidValue;
+    fn<<<dim3(nsplit, d.n_kv_heads, d.batch), kGenThreads, general_lds_bytes(d, keep, t), s>>>(
+            (const T*)q, (const T*)k_thin, (const T*)v_cache, seq_lens, kept_idx, d.seq_capacity,
+            d.n_kv_heads, d.n_q_heads / d.n_kv_heads, d.head_dim, keep, t.kp, t.ks, scale, chunk,
+            nsplit, rec, partials, stash);
+    return hipGetLastError();
 }
 
 }  // namespace thinkkv
