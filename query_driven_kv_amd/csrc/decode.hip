@@ -65,7 +65,6 @@ hipError_t static_scratch(void** ptr) {
 
 // defined in decode_mfma.hip
 bool mfma_decode_supported(const think_dims& d, int keep);
-int mfma_decode_chunk(const think_dims& d, int keep);
 hipError_t launch_decode_mfma(const think_dims& d, const DecodeGeom& g, const void* q,
                               const void* k_thin, const void* v_cache, const int32_t* seq_lens,
                               const int32_t* kept_idx, int keep, float scale, float* partials,
@@ -352,6 +351,37 @@ int general_chunk(const think_dims& d, int keep) {
     int chunk = kGenChunk;
     while (chunk > 64 && wgs(chunk / 2) <= resident) chunk /= 2;
     return chunk;
+}
+
+// Tokens per workgroup of the matrix-core chunk pass: a multiple of 128 (one
+// 32-token step per wave), sized for about 512 workgroups (two per CU) and at
+// most 256 chunks per sequence.  A batch of 2..64 sequences with 16-byte
+// aligned thin rows of at most 64 channels (an instance small enough for three
+// workgroups per CU) is sized for about 768: measured faster there (8 x 16K,
+// keep 64: 75.7 -> 71.7 us), while one sequence streams best at two per CU
+// (128K: 69 -> 71.5 us at 768).  Floor: 512 tokens (four steps per wave) for
+// those batches, so the prologue and the merge stay small next to the stream
+// (8 x 4K x 8 heads: 27.6 us, 31.2 at a 256 floor); for one sequence (or more
+// than 64) the floor is what gives about one workgroup per CU, between 128
+// and 512, so a small call still spreads over the chip (4K x 8 heads, keep 64:
+// 15.5 -> 12.2 us; 8K x 8 heads 16.0 -> 13.8; 4K x 32 heads keeps 512).
+int mfma_decode_chunk(const think_dims& d, int keep) {
+    const bool balanced = d.batch >= 2 && d.batch <= 64;
+    const bool three = balanced && keep % 8 == 0 && keep <= 64;
+    const int64_t wgs = three ? 768 : 512;
+    const int64_t work = (int64_t)d.seq_capacity * d.n_kv_heads * d.batch;
+    int64_t chunk = (work + wgs - 1) / wgs;
+    const int64_t min_chunk = ((int64_t)d.seq_capacity + 255) / 256;
+    if (chunk < min_chunk) chunk = min_chunk;
+    chunk = (chunk + 127) / 128 * 128;
+    int64_t floor = kDecodeMinChunk;
+    if (!balanced) {
+        floor = ((work + 255) / 256 + 127) / 128 * 128;
+        if (floor < kDecodeUnit) floor = kDecodeUnit;
+        if (floor > kDecodeMinChunk) floor = kDecodeMinChunk;
+    }
+    if (chunk < floor) chunk = floor;
+    return (int)chunk;
 }
 
 DecodeGeom decode_geom(const think_dims& d, int keep) {

@@ -553,26 +553,6 @@ bool mfma_decode_supported(const think_dims& d, int keep) {
            d.n_q_heads / d.n_kv_heads <= 16 && keep >= 1 && keep <= d.head_dim;
 }
 
-// Tokens per workgroup: a multiple of 128 (one 32-token step per wave), sized
-// for about 512 workgroups (two per CU) and at most 256 chunks per sequence,
-// and at least 512 (four steps per wave) so the prologue and the merge stay
-// small next to the stream when there are many kv heads and few tokens.  A
-// batch of 2..64 sequences with 16-byte aligned thin rows of at most 64
-// channels (an instance small enough for three workgroups per CU) is sized
-// for about 768: measured faster there (8 x 16K, keep 64: 75.7 -> 71.7 us),
-// while one sequence streams best at two per CU (128K: 69 -> 71.5 us at 768).
-int mfma_decode_chunk(const think_dims& d, int keep) {
-    const bool three = d.batch >= 2 && d.batch <= 64 && keep % 8 == 0 && keep <= 64;
-    const int64_t wgs = three ? 768 : 512;
-    const int64_t work = (int64_t)d.seq_capacity * d.n_kv_heads * d.batch;
-    int64_t chunk = (work + wgs - 1) / wgs;
-    const int64_t min_chunk = ((int64_t)d.seq_capacity + 255) / 256;
-    if (chunk < min_chunk) chunk = min_chunk;
-    chunk = (chunk + 127) / 128 * 128;
-    if (chunk < 512) chunk = 512;
-    return (int)chunk;
-}
-
 hipError_t launch_decode_mfma(const think_dims& d, const DecodeGeom& g, const void* q,
                               const void* k_thin, const void* v_cache, const int32_t* seq_lens,
                               const int32_t* kept_idx, int keep, float scale, float* partials,
