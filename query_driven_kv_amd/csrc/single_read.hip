@@ -33,10 +33,10 @@
 // advances, so graph replays differ too, with the call's own counter below
 // it), so a workspace with any previous contents works.  Every flag has one
 // writer, which stores it once the data it publishes (written through to
-// memory with device-scope stores) is complete; waiters read it with an
-// atomic add of zero, which the memory system performs on the current value
-// (a plain load kept returning a copy cached in this chiplet's L2), then take
-// one acquire fence.  (One arrival counter updated by every workgroup
+// memory with device-scope stores) is complete; waiters read it with a
+// relaxed agent-scope atomic load, which is a device-coherent (sc1) load that
+// reads past this chiplet's cached copy (ordinary loads returned a copy cached
+// in the chiplet's L2, 12 us late), then take one acquire fence.  (One arrival counter updated by every workgroup
 // serialised the arrivals: about 1 ms per call when tried.)  The grid is at
 // most one workgroup per compute unit and the occupancy query confirms that
 // one fits, so every workgroup is resident at once, or becomes resident as
@@ -76,16 +76,15 @@ __device__ __forceinline__ void signal_flag(unsigned long long* f, unsigned long
 
 // Wait until flags[0..n) all hold the tag (thread i watches flags i, i+512,
 // ...); the workgroup's later loads see everything their writers stored.  A
-// flag is read with an atomic add of zero, which the memory system performs
-// on the current value (a plain load can return a copy cached on this
-// chiplet); one acquire fence for the workgroup after the waits.
+// flag is read with a relaxed agent-scope atomic load (a device-coherent sc1
+// load: an ordinary load can return a copy cached on this chiplet); one
+// acquire fence for the workgroup after the waits.
 __device__ __forceinline__ void wait_flags(unsigned long long* f, int n,
                                            unsigned long long tag, unsigned long long want,
                                            uint32_t limit, unsigned long long* err) {
     for (int i = threadIdx.x; i < n; i += blockDim.x) {
         for (uint32_t spin = 0;; ++spin) {
-            if (__hip_atomic_fetch_add(f + i, 0ull, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT) == want)
+            if (__hip_atomic_load(f + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == want)
                 break;
             if (spin >= limit) {
                 __hip_atomic_store(err, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -346,8 +345,7 @@ __global__ __launch_bounds__(kSrThreads) void k_score_compact_resident(SrParams 
         for (int i = tid; i < p.Hkv * nw; i += kSrThreads) {
             unsigned long long x = 0;
             for (uint32_t spin = 0;; ++spin) {
-                x = __hip_atomic_fetch_add(words + i, 0ull, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
+                x = __hip_atomic_load(words + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 if ((x >> 16) == want) break;
                 if (spin >= p.spin_limit) {
                     __hip_atomic_store(p.err, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
