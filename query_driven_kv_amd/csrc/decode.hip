@@ -286,7 +286,8 @@ GeneralTile general_tile(const think_dims& d, int keep) {
     GeneralTile t{};
     const int e = d.dtype == THINK_F32 ? 4 : 2;
     const int D = d.head_dim;
-    t.kb = keep * e % 16 == 0 ? 16 : e;
+    const int row = keep * e;                    // bytes of a thin row
+    t.kb = row % 16 == 0 ? 16 : row % 8 == 0 ? 8 : row % 4 == 0 && e == 2 ? 4 : e;
     t.gm = d.n_q_heads / d.n_kv_heads <= 4 ? 4 : kGenMaxG;
     auto vr_for = [&](int tt) {
         const int tgs = kGenThreads / (D / 4);
@@ -295,7 +296,7 @@ GeneralTile general_tile(const think_dims& d, int keep) {
     auto kr_for = [&](int tt) {
         const int units = tt * (keep * e / t.kb);
         const int k = pow2_at_least((units + kGenThreads - 1) / kGenThreads);
-        return t.kb == 16 ? k : (k < 8 ? 8 : k);
+        return t.kb == 16 ? k : t.kb > e ? (k < 4 ? 4 : k) : (k < 8 ? 8 : k);
     };
     t.tt = 32;
     if (t.kb == 16) {

@@ -10,9 +10,9 @@
 // Per tile:
 //  * its thin key rows of this head (keep contiguous elements at the token
 //    stride Hkv*keep) are loaded in units of KB bytes, consecutive lanes on
-//    consecutive units (16-byte units when keep * elem_bytes is a multiple of
-//    16, which keeps every unit inside one aligned row; else one element),
-//    and stored to LDS as fp32;
+//    consecutive units: the largest of 16, 8 and 4 bytes that divides a row
+//    (so every unit lies inside one row, aligned), else one element; stored
+//    to LDS as fp32;
 //  * its value rows (D contiguous elements, 16-byte aligned) are loaded as
 //    4-element quads straight into registers;
 //  * logits: LP = 256 / TT lanes per token; lane p sums the 4-channel chunks
@@ -99,12 +99,10 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // Ring depth from the registers one tile takes (key units + value quads).
-// One-element key units (rows that are not whole 16-byte units) keep the
-// plain double buffer.
 template <int DT, int VR, int KB, int KR>
 constexpr int ring_depth() {
     constexpr int regs = KR * (KB >= 4 ? KB / 4 : 1) + VR * (DT == THINK_F32 ? 4 : 2);
-    return KB != 16 ? 2 : regs <= 8 ? 4 : regs <= 16 ? 3 : 2;
+    return regs <= 8 ? 4 : regs <= 16 ? 3 : 2;
 }
 
 template <int DT, int TT, int VR, int KB, int KR, int GM>
@@ -196,6 +194,12 @@ __global__ __launch_bounds__(kGenThreads) void k_decode_general(
                 kd[i][1] = w.y;
                 kd[i][2] = w.z;
                 kd[i][3] = w.w;
+            } else if constexpr (KB == 8) {
+                const unsigned long long w = __builtin_bit_cast(
+                        unsigned long long,
+                        __builtin_amdgcn_raw_buffer_load_b64(rk, (int)off, 0, kNonTemporal));
+                kd[i][0] = (uint32_t)w;
+                kd[i][1] = (uint32_t)(w >> 32);
             } else if constexpr (KB == 4) {
                 kd[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rk, (int)off, 0, kNonTemporal);
             } else {
@@ -420,11 +424,12 @@ using GeneralKernel = void (*)(const typename Elem<DT>::T*, const typename Elem<
                                int32_t*);
 
 // The instance for a tile shape (nullptr for a shape no instance covers).
-// Only the (TT, VR, KR) combinations that keep <= head_dim <= 256 can reach
-// are built: 32-token tiles take 16-byte key units numbering
-// ceil(keep * e / 128) a thread, at most VR (fp32) or VR / 2 (bf16), or
-// one-element units numbering ceil(keep / 8), at most 4 * VR (8 when VR <=
-// 2); 64-token tiles are chosen only with 16-byte units, VR <= 4 and KR <= 2.
+// Only the (TT, VR, KB, KR) combinations that keep <= head_dim <= 256 can
+// reach are built.  32-token tiles: 16-byte key units number
+// ceil(keep * e / 128) a thread, at most VR (fp32) or VR / 2 (bf16); 8- and
+// 4-byte units (taken at KR 4, 8 or 16) at most 2 VR; one-element units
+// ceil(keep / 8), at most 4 * VR (8 when VR <= 2).  64-token tiles are chosen
+// only with 16-byte units, VR <= 4 and KR <= 2.
 template <int DT>
 GeneralKernel<DT> general_kernel(const GeneralTile& t) {
     auto pick = [&](auto ttc, auto vrc, auto kbc, auto krc) -> GeneralKernel<DT> {
@@ -444,6 +449,7 @@ GeneralKernel<DT> general_kernel(const GeneralTile& t) {
     auto tile32 = [&](auto vrc) -> GeneralKernel<DT> {
         constexpr int VR = decltype(vrc)::value;
         constexpr int kmax16 = DT == THINK_F32 ? VR : (VR > 1 ? VR / 2 : 1);
+        constexpr int kmax84 = 2 * VR < 4 ? 4 : 2 * VR;
         constexpr int kmax1 = VR > 2 ? 4 * VR : 8;
         if (t.kb == 16) {
             if (t.kr > kmax16) return nullptr;
@@ -451,6 +457,17 @@ GeneralKernel<DT> general_kernel(const GeneralTile& t) {
             if constexpr (kmax16 >= 4) if (t.kr == 4) return pick(I32{}, vrc, I16{}, I4{});
             if constexpr (kmax16 >= 2) if (t.kr == 2) return pick(I32{}, vrc, I16{}, I2{});
             return pick(I32{}, vrc, I16{}, I1{});
+        }
+        if (t.kb == 8 || (t.kb == 4 && DT == THINK_BF16)) {
+            if (t.kr > kmax84) return nullptr;
+            auto by_kr = [&](auto kbc) -> GeneralKernel<DT> {
+                if constexpr (kmax84 >= 16) if (t.kr == 16) return pick(I32{}, vrc, kbc, I16{});
+                if constexpr (kmax84 >= 8) if (t.kr == 8) return pick(I32{}, vrc, kbc, I8{});
+                return pick(I32{}, vrc, kbc, I4{});
+            };
+            if (t.kb == 8) return by_kr(I8{});
+            if constexpr (DT == THINK_BF16) return by_kr(I4{});
+            return nullptr;
         }
         if (t.kr > kmax1) return nullptr;
         if constexpr (kmax1 >= 32) if (t.kr == 32) return pick(I32{}, vrc, KE{}, I32{});
