@@ -63,6 +63,8 @@ def parse():
                     help="skip the append, append+decode and prefill figures")
     ap.add_argument("--parity", action="store_true",
                     help="with --no-cpu-baseline: still check layer 0 against the oracle")
+    ap.add_argument("--no-decode-shapes", action="store_true",
+                    help="leave out the decode-alone figures of the general-path shapes")
     ap.add_argument("--decode-shape", action="append", default=[],
                     metavar="DTYPE,B,HQ,HKV,D,S,KEEP",
                     help="instead of the workload: time the decode alone (chunk pass + "
@@ -409,6 +411,13 @@ def probe_ceiling(torch, dev, read_bytes, write_bytes, launches=64):
     us = e0.elapsed_time(e1) * 1e3 / launches
     del src, dst
     return us
+
+
+# decode-alone shapes reported in the default line: 32K tokens x 8 kv heads,
+# fp32 D 128 keep 64 and bf16 D 256 keep 128 (general chunk pass), bf16 D 64
+# keep 32 (matrix-core kernel, head_dim 64)
+DECODE_SHAPES = ("f32,1,32,8,128,32768,64", "bf16,1,16,8,256,32768,128",
+                 "bf16,1,32,8,64,32768,32")
 
 
 def decode_shape_bench(spec, torch, dev, calls=200):
@@ -906,6 +915,16 @@ def main():
             result["also"][name] = r2
             del wl2
             torch.cuda.empty_cache()
+    # decode alone on 32K shapes that take the general chunk pass (fp32, bf16
+    # head_dim 256) or the matrix-core kernel's head_dim-64 instance
+    if not args.no_decode_shapes:
+        if "wl" in locals():
+            del wl
+        torch.cuda.empty_cache()
+        result["decode_shapes"] = []
+        for spec in DECODE_SHAPES:
+            log(f"decode shape {spec}")
+            result["decode_shapes"].append(decode_shape_bench(spec, torch, dev))
     print(json.dumps(result), flush=True)
 
 
