@@ -89,7 +89,12 @@ THINK_API int32_t think_keep_from_ratio(int32_t head_dim, double prune_ratio);
 
 /* Bytes of device workspace think_score needs for these dims; 0 if invalid. */
 THINK_API size_t think_score_workspace_bytes(const think_dims *d);
-/* Bytes of device workspace think_decode_attn needs; 0 if invalid. */
+/* Bytes of device workspace think_decode_attn needs; 0 if invalid.  For
+ * shapes the bf16 matrix-core kernel does not take (fp32, other head dims)
+ * the size follows the token chunk, which is chosen from the current
+ * device's compute units and the kernel's occupancy: ask on the device the
+ * calls will run on (on a host without a device the answer assumes 256-token
+ * chunks). */
 THINK_API size_t think_decode_workspace_bytes(const think_dims *d, int32_t keep);
 
 /*

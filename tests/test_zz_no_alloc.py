@@ -1,8 +1,9 @@
 """The allocation-free decode (think_decode_attn_static), called through the C
 ABI: its output equals think_decode_attn's (same kernels, bitwise) and lies
-within the bf16 bound of the oracle, on two calls in a row on the device's one
-scratch array, the second with a smaller input; a shape whose records exceed
-the array is refused before anything is enqueued."""
+within the dtype's bound of the oracle, on calls in a row on the device's one
+scratch array, each with a smaller input than the one before (bf16 on the
+matrix-core kernel, then fp32 on the general one); a shape whose records
+exceed the array is refused before anything is enqueued."""
 import ctypes
 
 import numpy as np
@@ -50,13 +51,17 @@ def test_static_scratch_decode_matches_the_workspace_call():
     small = kvsynth.custom("no-alloc-small", batch=3, n_q_heads=8, n_kv_heads=2, head_dim=128,
                            seq_capacity=700, obs_window=8, keep=51, dtype="bf16", lowrank=8,
                            ragged=(200, 700), cfg_id=77)
-    for cfg, step in ((big, 0), (small, 1)):
-        print(f"[no-alloc] {cfg.name}: B={cfg.batch} S={cfg.seq_capacity} keep={cfg.keep}",
-              flush=True)
+    general = kvsynth.custom("no-alloc-f32", batch=2, n_q_heads=8, n_kv_heads=2, head_dim=64,
+                             seq_capacity=600, obs_window=8, keep=30, dtype="f32", lowrank=8,
+                             ragged=(100, 600), cfg_id=78)
+    for cfg, step in ((big, 0), (small, 1), (general, 2)):
+        print(f"[no-alloc] {cfg.name}: B={cfg.batch} S={cfg.seq_capacity} keep={cfg.keep} "
+              f"{cfg.dtype}", flush=True)
         got, ref, o_ref = _decode_pair(cfg, 0, step)
         np.testing.assert_array_equal(got.view(np.uint8), ref.view(np.uint8))
         err = row_rel_err(got, o_ref).max()
-        assert err <= 2e-2, f"{cfg.name}: row error {err:.3e}"
+        bar = 2e-2 if cfg.dtype == "bf16" else 1e-5
+        assert err <= bar, f"{cfg.name}: row error {err:.3e}"
 
 
 def test_static_scratch_refuses_shapes_past_its_size():
