@@ -301,7 +301,7 @@ GeneralTile general_tile(const think_dims& d, int keep) {
     t.tt = 32;
     if (t.kb == 16) {
         const int vr = vr_for(64), kr = kr_for(64);
-        if (vr <= 4 && kr <= 2 && kr * 4 + vr * (e == 4 ? 4 : 2) <= 24) t.tt = 64;
+        if (vr <= (e == 2 ? 8 : 4) && kr <= 2 && kr * 4 + vr * (e == 4 ? 4 : 2) <= 24) t.tt = 64;
     }
     t.vr = vr_for(t.tt);
     t.kr = kr_for(t.tt);

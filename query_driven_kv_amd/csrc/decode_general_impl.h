@@ -429,7 +429,7 @@ using GeneralKernel = void (*)(const typename Elem<DT>::T*, const typename Elem<
 // ceil(keep * e / 128) a thread, at most VR (fp32) or VR / 2 (bf16); 8- and
 // 4-byte units (taken at KR 4, 8 or 16) at most 2 VR; one-element units
 // ceil(keep / 8), at most 4 * VR (8 when VR <= 2).  64-token tiles are chosen
-// only with 16-byte units, VR <= 4 and KR <= 2.
+// only with 16-byte units, KR <= 2 and VR <= 4 (VR 8 for bf16).
 template <int DT>
 GeneralKernel<DT> general_kernel(const GeneralTile& t) {
     auto pick = [&](auto ttc, auto vrc, auto kbc, auto krc) -> GeneralKernel<DT> {
@@ -480,6 +480,9 @@ GeneralKernel<DT> general_kernel(const GeneralTile& t) {
     };
     if (t.tt == 64) {
         switch (t.vr) {
+            case 8:                              // bf16 only (8 quads of 8 bytes)
+                if constexpr (DT == THINK_BF16) return tile64(I8{});
+                return nullptr;
             case 4: return tile64(I4{});
             case 2: return tile64(I2{});
             case 1: return tile64(I1{});
