@@ -50,7 +50,8 @@ def parse():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (hardware-counter scaling)")
     ap.add_argument("--no-kernel-timing", action="store_true",
-                    help="skip the per-launch event pass (hardware-counter runs)")
+                    help="skip the per-launch event pass and the graph replay "
+                         "(hardware-counter runs)")
     ap.add_argument("--decode-steps", type=int, default=0,
                     help="override the workload's decode steps (profiling runs only; "
                          "reported in config)")
@@ -723,7 +724,8 @@ def measure(cfg, args, torch, qdk, dev, steps, warmup, extras):
 
     ms_per_step = wall / steps * 1e3
     # small steps: the same step replayed from a graph, without host launch gaps
-    graph_ms = graph_step_ms(wl, torch) if ms_per_step < 5.0 else None
+    graph_ms = (graph_step_ms(wl, torch) if ms_per_step < 5.0 and not args.no_kernel_timing
+                else None)
     if graph_ms is not None:
         log(f"{cfg.name}: graph-replayed step {graph_ms * 1e3:.1f} us")
     sc_moved = bm["sc_min_layer"] if wl.single_read else bm["sc_layer"]
