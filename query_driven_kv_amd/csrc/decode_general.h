@@ -17,7 +17,7 @@ namespace thinkkv {
 
 constexpr int kGenThreads = 256;   // threads per workgroup
 constexpr int kGenChunk = 256;     // tokens per workgroup (one chunk slot), halved down to 64
-                                   // while a call has fewer than 1024 workgroups
+                                   // while the halved grid still fits the GPU's resident workgroups
 constexpr int kGenMaxG = 16;       // query heads per kv head
 
 // Logits and running maxima of fp32 inputs are kept in fp64: with fp32 inputs
@@ -32,7 +32,8 @@ using LogitT = typename std::conditional<DT == THINK_F32, double, float>::type;
 struct GeneralTile {
     int tt;    // tokens per tile: 32, or 64 when a tile's loads fit in few registers
     int vr;    // value quads per thread and tile
-    int kb;    // key unit bytes: 16 when keep * elem_bytes is a multiple of 16, else one element
+    int kb;    // key unit bytes: the largest of 16, 8 (and 4 for bf16) dividing keep * elem_bytes,
+               // else one element
     int kr;    // key units per thread and tile
     int gm;    // head slots: 4 or 16
     int kp;    // keep rounded up to whole 4-channel chunks per logit lane

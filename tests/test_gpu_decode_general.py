@@ -6,7 +6,7 @@ oracle's decode on the same bytes.
 
 Shape classes the random draws cover (the launcher picks them from dtype,
 head_dim, keep and the query heads per kv head): 32- and 64-token tiles,
-16-byte and one-element key units, 4 and 16 head slots, chunks of 256 tokens
+16-, 8- and 4-byte and one-element key units, 4 and 16 head slots, chunks of 256 tokens
 halved while the grid fits one wave of resident workgroups.  Padding rows of
 K_thin and V past each length hold NaN, so a read past len_b shows up.
 Bar: per row max-abs error relative to the row's max-abs, 1e-5 (fp32) and
