@@ -2,7 +2,9 @@
 """Throughput of the key-channel pruning hot path on one MI355X.
 
 One step = the whole path over one batch of synthetic input:
-  for every layer: think_score_select (scores + kept channels) -> think_compact_k
+  for every layer: think_score_select_compact (scores, kept channels and the
+    thin key cache: one launch that reads K once where the cache fits the
+    register files, else the score pass and the compaction)
   then for every decode step and every layer: think_decode_attn
 Default workload: the 32-layer LLaMA-3-8B-like cache, 131072 tokens per
 layer, 32 q / 8 kv heads, head_dim 128, window 64, keep 64 of 128 (bf16),
@@ -13,7 +15,9 @@ the 8 TB/s peak, and KV tokens per second.  Algorithmic bytes:
   score+compact, per layer : 2|K| + |K_thin| + |Q_w|   (two streaming reads of K)
   decode, per call          : |K_thin| + |V| + |q| + |out|
 with |X| counted over valid tokens.  Inputs are resident in HBM before the
-timed region.  Prints one JSON line.
+timed region.  The timed steps run back to back between two synchronisations
+(wall clock); the per-path figures, the chunk pass's launch duration and the
+graph replay come from passes after it.  Prints one JSON line.
 """
 import argparse
 import ctypes
@@ -50,7 +54,7 @@ def parse():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (hardware-counter scaling)")
     ap.add_argument("--no-kernel-timing", action="store_true",
-                    help="skip the per-launch event pass and the graph replay "
+                    help="skip the chunk-pass timing passes and the graph replay "
                          "(hardware-counter runs)")
     ap.add_argument("--decode-steps", type=int, default=0,
                     help="override the workload's decode steps (profiling runs only; "
@@ -189,10 +193,14 @@ class Workload:
                 yield self.dec_args[c][s][l]
 
     def decode_kernel_times(self, stream, torch, min_launches=64):
-        """One step's decode calls (repeated until at least `min_launches`) in
-        split-phase form, with HIP events on the launch stream around every
-        chunk-pass launch: the chunk pass's mean launch duration in
-        microseconds, the launch count and the 10/50/90th percentiles."""
+        """The chunk pass's launch duration, live, in split-phase form: one
+        step's decode calls (repeated until at least `min_launches`) as chunk
+        passes alone, back to back between two HIP events on the launch stream
+        (mean microseconds per launch: the kernel plus the dispatch gap to the
+        next); then the same calls with the merge between them and events
+        around every chunk pass (10/50/90th percentiles; an event record on
+        the stream adds a few microseconds to what it brackets).  Returns
+        (mean, launches, percentiles)."""
         from query_driven_kv_amd import _lib
         lib, P = _lib.lib, ctypes.c_void_p
         d, keep = ctypes.byref(self.dims), self.cfg.keep
@@ -200,21 +208,45 @@ class Workload:
         per_step = self.cfg.decode_steps * self.cfg.layers
         passes = max(1, -(-min_launches // per_step))
         n = passes * per_step
+        calls = [c for _ in range(passes) for c in self.decode_calls()]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for (q, thin, v, lens, idx) in calls:
+            _lib.check("think_decode_attn_partial", lib.think_decode_attn_partial(
+                d, q, thin, v, lens, idx, keep, self.scale, ws, wsn, stream))
+        e1.record()
+        torch.cuda.synchronize()
+        mean_us = e0.elapsed_time(e1) * 1e3 / n
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(n)]
         calls = [c for _ in range(passes) for c in self.decode_calls()]
-        k = 0
-        for (q, thin, v, lens, idx) in calls:
+        for k, (q, thin, v, lens, idx) in enumerate(calls):
             ev[k][0].record()
             _lib.check("think_decode_attn_partial", lib.think_decode_attn_partial(
                 d, q, thin, v, lens, idx, keep, self.scale, ws, wsn, stream))
             ev[k][1].record()
             _lib.check("think_decode_attn_combine", lib.think_decode_attn_combine(
                 d, lens, keep, out, ws, wsn, stream))
-            k += 1
         torch.cuda.synchronize()
         us = np.array([a.elapsed_time(b) for a, b in ev]) * 1e3
-        return float(us.mean()), n, [round(float(x), 2) for x in np.percentile(us, [10, 50, 90])]
+        return mean_us, n, [round(float(x), 2) for x in np.percentile(us, [10, 50, 90])]
+
+    def path_ms(self, stream, torch, rounds):
+        """Milliseconds per step of each path on its own: `rounds` steps' worth
+        of score+compact calls back to back between two HIP events, then as
+        many steps' decode calls (the copy rotation carries on)."""
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        torch.cuda.synchronize()
+        e[0].record()
+        for _ in range(rounds):
+            self.score_compact(stream)
+        e[1].record()
+        for _ in range(rounds):
+            self.decode(stream)
+        e[2].record()
+        torch.cuda.synchronize()
+        return e[0].elapsed_time(e[1]) / rounds, e[1].elapsed_time(e[2]) / rounds
 
     def decode(self, stream, steps=None):
         from query_driven_kv_amd import _lib
@@ -424,8 +456,8 @@ DECODE_SHAPES = ("f32,1,32,8,128,32768,64", "bf16,1,16,8,256,32768,128",
 def decode_shape_bench(spec, torch, dev, calls=200):
     """Decode alone on one synthetic shape "dtype,B,Hq,Hkv,D,S,keep" with every
     sequence at full length: mean time per think_decode_attn call (chunk pass
-    + combine, back to back), the chunk pass's mean launch duration (events
-    around each launch in split-phase form), algorithmic GB/s and the
+    + combine, back to back), the chunk pass's mean launch duration (64 chunk
+    passes alone, back to back between two events), algorithmic GB/s and the
     single-launch ceiling for the call's bytes.  Inputs are N(0, 1) drawn on
     the device, in enough copies (rotated call to call) that the reads come
     from HBM."""
@@ -471,17 +503,14 @@ def decode_shape_bench(spec, torch, dev, calls=200):
     e1.record()
     torch.cuda.synchronize()
     us_call = e0.elapsed_time(e1) * 1e3 / calls
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(64)]
-    for k, (a, b) in enumerate(ev):
-        a.record()
+    nchunk = 64
+    e0.record()
+    for k in range(nchunk):
         _lib.check("think_decode_attn_partial", lib.think_decode_attn_partial(
             d, *args[k % ncopies], keep, scale, P(ws.data_ptr()), wsn, sp))
-        b.record()
-        _lib.check("think_decode_attn_combine", lib.think_decode_attn_combine(
-            d, P(lens.data_ptr()), keep, P(out.data_ptr()), P(ws.data_ptr()), wsn, sp))
+    e1.record()
     torch.cuda.synchronize()
-    us_chunk = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    us_chunk = e0.elapsed_time(e1) * 1e3 / nchunk
     rd = B * S * Hkv * (keep + D) * e + B * Hq * D * e
     wr = B * Hq * D * e
     del kt, v
@@ -511,13 +540,13 @@ def decode_source_hash():
 
 def committed_traffic(workload):
     """HBM bytes per chunk-pass launch from the committed hardware-counter
-    summary, if it was taken on this workload with the current kernel source."""
-    path = os.path.join(ROOT, "profiles", "decode_mfma_llama3-8b-128k_counters.json")
+    summary of this workload, if it was taken with the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"decode_mfma_{workload}_counters.json")
     try:
         with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
-        return None, "no counter summary"
+        return None, "no counter summary for this workload"
     if rec.get("workload") != workload:
         return None, "counters taken on another workload"
     if rec.get("source_hash") != decode_source_hash():
@@ -704,23 +733,19 @@ def measure(cfg, args, torch, qdk, dev, steps, warmup, extras):
     torch.cuda.synchronize()
     log(f"{cfg.name}: warmup done")
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(steps):
-        a, b, c = ev[k]
-        a.record(stream)
+    for _ in range(steps):
         wl.score_compact(sp)
-        b.record(stream)
         wl.decode(sp)
-        c.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    sc_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
-    dec_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
-    log(f"{cfg.name}: timed {steps} steps: {wall:.3f}s wall, score+compact {sc_ms:.3f} ms, "
-        f"decode {dec_ms:.3f} ms per step")
+    log(f"{cfg.name}: timed {steps} steps: {wall:.3f}s wall")
+    # each path alone, after the timed region: `steps` rounds of one path's
+    # calls back to back between two events (events inside the timed loop
+    # would each add a few microseconds of stream time to a small step)
+    sc_ms, dec_ms = wl.path_ms(sp, torch, steps)
+    log(f"{cfg.name}: per path: score+compact {sc_ms:.3f} ms, decode {dec_ms:.3f} ms per step")
 
     ms_per_step = wall / steps * 1e3
     # small steps: the same step replayed from a graph, without host launch gaps
@@ -796,10 +821,12 @@ def measure(cfg, args, torch, qdk, dev, steps, warmup, extras):
                      "frac": round(achieved / PEAK_GBS, 4) if achieved else None,
                      "algorithmic_bytes_per_launch": bm["dec_call"],
                      "launch_us": round(part_us, 2) if n_part else None,
-                     "launch_us_p10_p50_p90": part_pct,
-                     "timing": (f"HIP events on the launch stream around each of {n_part} "
-                                f"chunk-pass launches (one step's decode calls, repeated to at "
-                                f"least 64), after the timed steps")},
+                     "event_pair_launch_us_p10_p50_p90": part_pct,
+                     "timing": (f"{n_part} chunk-pass launches (one step's decode calls, "
+                                f"repeated to at least 64) back to back between two HIP events "
+                                f"on the launch stream, after the timed steps; the percentiles "
+                                f"are of the same launches timed one by one between the merges, "
+                                f"an event pair around each")},
         "near_ties": near,
         "input_copies": wl.ncopies,
         "ceiling": {
@@ -945,6 +972,7 @@ def main():
         for name in also:
             c2 = kvsynth.CONFIGS[name]
             wl2, r2 = measure(c2, args, torch, qdk, dev, args.also_steps, 3, extras=False)
+            r2["roofline"]["traffic"], r2["roofline"]["traffic_source"] = committed_traffic(name)
             g2 = gpu_layer0(wl2, torch)
             if not args.no_cpu_baseline or args.parity:
                 _, ref2 = oracle_sample(wl2, 0.0, len(os.sched_getaffinity(0)))
