@@ -78,11 +78,18 @@ int pow2_at_least(int n) {
     return p;
 }
 
-// Merge the chunks of one (b, h).  The block is (D/4) x SG threads, each
-// thread owning four output columns (one 16-byte record load per slot):
+// Merge the chunks of one (b, h), or of one slice of its output columns
+// (blockIdx.z of gridDim.z equal slices of D/4 column quads: each slice
+// reads the slots' maxima and sums and its own columns of the records, so a
+// head whose records run to many kilobytes is pulled in by several compute
+// units; every column's arithmetic is the same in any slicing).  The block is
+// (D/4/slices) x SG threads, each thread owning four output columns (one
+// 16-byte record load per slot):
 // sub-group sg merges a contiguous range of the nsplit chunk slots in
 // ascending order, eight at a time with a running maximum, then the SG results
-// are merged in ascending sg order.  Fixed order, so the result is bitwise
+// are merged pairwise in a fixed tree (log2 SG rounds; merged one after
+// another by the first sub-group, 32 of them cost 3.2 us a call: D 256 at
+// 32K tokens, 40.5 -> 37.2 us).  Fixed order, so the result is bitwise
 // reproducible.  Fixed and per-sequence chunks: the ranges are fixed by nsplit
 // rather than by the length, so the record loads do not wait for the length
 // load; slots at or past the sequence's chunk count are dropped after loading
@@ -103,8 +110,9 @@ __global__ __launch_bounds__(1024) void k_decode_combine(
     constexpr MT kNone = -3.402823466e38f;      // finite stand-in for an empty maximum
     const int h = blockIdx.x, b = blockIdx.y, Hq = gridDim.x, nb = gridDim.y;
     const int tid = threadIdx.x;
-    const int D4 = D >> 2;
+    const int D4 = (D >> 2) / gridDim.z;         // column quads of this slice
     const int d4 = tid % D4, sg = tid / D4;
+    const int q4 = blockIdx.z * D4 + d4;         // the thread's column quad in the row
     const float* base = partials + ((size_t)b * Hq + h) * nsplit * rec;
     const int32_t* lens = ap.stash ? ap.stash : seq_lens;
     int nrange = nsplit, used = 0;               // slots in the ranges; used: balanced only
@@ -143,7 +151,7 @@ __global__ __launch_bounds__(1024) void k_decode_combine(
                 mk[k] = h2.x;
                 lk[k] = h2.y;
             }
-            ov[k] = *reinterpret_cast<const float4*>(r + 4 + 4 * d4);
+            ov[k] = *reinterpret_cast<const float4*>(r + 4 + 4 * q4);
         }
         // the record loads above are issued before the length is waited on
         asm volatile("" : "+s"(len_raw)::"memory");
@@ -204,13 +212,37 @@ __global__ __launch_bounds__(1024) void k_decode_combine(
             s_prod[j] = prod;
         }
     }
-    if (d4 == 0) {
-        sM[sg] = M;
-        sL[sg] = L;
+    // the sub-groups' results merged pairwise in a fixed tree: in the round of
+    // stride st, sub-group sg (a multiple of 2 st) takes sub-group sg + st,
+    // each thread keeping its own state in registers.  A round's senders
+    // publish slots that no unfinished reader of an earlier round uses, so
+    // one barrier a round suffices.
+    for (int st = 1; st < sg_count; st *= 2) {
+        if (sg % (2 * st) == st) {
+            if (d4 == 0) {
+                sM[sg] = M;
+                sL[sg] = L;
+            }
+            sO[tid] = O;
+        }
+        __syncthreads();
+        if (sg % (2 * st) == 0 && sg + st < sg_count) {
+            const MT Mb = sM[sg + st];
+            const float Lb = sL[sg + st];
+            const float4 Ob = sO[tid + st * D4];
+            const MT Mn = Mb > M ? Mb : M;
+            const float fa = L > 0.0f ? expf((float)(M - Mn)) : 0.0f;
+            const float fb = Lb > 0.0f ? expf((float)(Mb - Mn)) : 0.0f;
+            L = fmaf(fa, L, fb * Lb);
+            O.x = fmaf(fa, O.x, fb * Ob.x);
+            O.y = fmaf(fa, O.y, fb * Ob.y);
+            O.z = fmaf(fa, O.z, fb * Ob.z);
+            O.w = fmaf(fa, O.w, fb * Ob.w);
+            M = Mn;
+        }
     }
-    sO[tid] = O;
-    __syncthreads();
     if (ap.stash) {                              // uniform: a kernel argument
+        __syncthreads();                         // s_prod complete
         if (tid < 4) {
             MT t = 0;
             for (int i = 0; i < 64; ++i) t += s_prod[tid * 64 + i];
@@ -219,25 +251,15 @@ __global__ __launch_bounds__(1024) void k_decode_combine(
         __syncthreads();
     }
     if (sg == 0) {
-        MT MM = sM[0];
-        for (int r = 1; r < sg_count; ++r) MM = sM[r] > MM ? sM[r] : MM;
-        float LL = 0.0f;
-        float4 OO = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int r = 0; r < sg_count; ++r) {
-            const float f = sL[r] > 0.0f ? expf((float)(sM[r] - MM)) : 0.0f;
-            const float4 o = sO[r * D4 + d4];
-            LL = fmaf(f, sL[r], LL);
-            OO.x = fmaf(f, o.x, OO.x);
-            OO.y = fmaf(f, o.y, OO.y);
-            OO.z = fmaf(f, o.z, OO.z);
-            OO.w = fmaf(f, o.w, OO.w);
-        }
+        const MT MM = M;
+        float LL = L;
+        float4 OO = O;
         if (app) {
             const MT lnew = (((s_dot[0] + s_dot[1]) + s_dot[2]) + s_dot[3]) * (MT)ap.scale;
             const MT Mf = lnew > MM ? lnew : MM;
             const float a = LL > 0.0f ? expf((float)(MM - Mf)) : 0.0f;
             const float wn = expf((float)(lnew - Mf));
-            const size_t v0 = ((size_t)b * Hkv + kv) * D + 4 * d4;
+            const size_t v0 = ((size_t)b * Hkv + kv) * D + 4 * q4;
             const typename E::T* vn = (const typename E::T*)ap.v_new;
             LL = fmaf(LL, a, wn);
             OO.x = fmaf(OO.x, a, wn * E::load(vn, v0 + 0));
@@ -246,15 +268,15 @@ __global__ __launch_bounds__(1024) void k_decode_combine(
             OO.w = fmaf(OO.w, a, wn * E::load(vn, v0 + 3));
         }
         const bool any = LL > 0.0f;
-        const size_t o0 = ((size_t)b * Hq + h) * D + 4 * d4;
+        const size_t o0 = ((size_t)b * Hq + h) * D + 4 * q4;
         E::store(out, o0 + 0, any ? OO.x / LL : 0.0f);
         E::store(out, o0 + 1, any ? OO.y / LL : 0.0f);
         E::store(out, o0 + 2, any ? OO.z / LL : 0.0f);
         E::store(out, o0 + 3, any ? OO.w / LL : 0.0f);
     }
     // fused append: the new token's rows (one workgroup per kv head) and the
-    // advanced length
-    if (app) {
+    // advanced length, from the first column slice
+    if (app && blockIdx.z == 0) {
         using T = typename E::T;
         if (h % (Hq / Hkv) == 0) {
             const int32_t* idx = ap.kept_idx + ((size_t)b * Hkv + kv) * ap.keep;
@@ -385,6 +407,22 @@ int mfma_decode_chunk(const think_dims& d, int keep) {
     return (int)chunk;
 }
 
+// Column slices of the merge: doubled while one head's records (its chunk
+// slots times the record size) exceed 16 KiB a slice, as long as the slices
+// divide the D/4 column quads and keep at least 8 of them (32 columns).  One
+// compute unit pulls records in at a few tens of GB/s; at 32K tokens slicing
+// took 0.3-1.1 us off a call (D 256, 266 KiB of records a head: 41.6 -> 40.5
+// us), and with the tree merge below 0.9-4.4 us.
+constexpr int64_t kCombineSliceBytes = 16 * 1024;
+
+static int combine_slices(const think_dims& d, const DecodeGeom& g) {
+    const int q4 = d.head_dim / 4;
+    const int64_t bytes = (int64_t)g.nsplit * g.rec * (int64_t)sizeof(float);
+    int n = 1;
+    while (bytes > kCombineSliceBytes * n && q4 % (2 * n) == 0 && q4 / (2 * n) >= 8) n *= 2;
+    return n;
+}
+
 DecodeGeom decode_geom(const think_dims& d, int keep) {
     DecodeGeom g{};
     g.mfma = mfma_decode_supported(d, keep);
@@ -427,11 +465,12 @@ hipError_t launch_decode_combine(const think_dims& d, const DecodeGeom& g, const
                                  hipStream_t s) {
     AppendArgs ap{};
     if (app) ap = *app;
-    dim3 cgrid(d.n_q_heads, d.batch);
+    const int slices = combine_slices(d, g);
+    dim3 cgrid(d.n_q_heads, d.batch, slices);
     // sub-groups: at least min(16, 1024 / D), and enough that each merges at
     // most 8 chunk slots (one batch of record loads in flight), within 1024
     // threads
-    const int d4 = d.head_dim / 4;
+    const int d4 = d.head_dim / 4 / slices;
     int sg_count = 1024 / d.head_dim;
     if (sg_count > 16) sg_count = 16;
     const int sg_slots = (g.nsplit + 7) / 8;
