@@ -4,18 +4,22 @@
 // (a launch of ~100 MB cannot reach the sustained bandwidth of a long stream:
 // the launch ramp and the drain of the last workgroups weigh on it).
 //
-// 512 workgroups of 512 threads (two per compute unit); workgroup w reads the
-// w-th of 512 contiguous slices of the source with 16-byte non-temporal buffer
-// loads, eight in flight per thread, and writes the w-th slice of the
-// destination with 16-byte non-temporal stores of values that depend on what
-// it read (so no load can be dropped).
+// 2048 workgroups of 512 threads; workgroup w reads the w-th of 2048
+// contiguous slices of the source with 16-byte non-temporal buffer loads,
+// eight in flight per thread, and writes the w-th slice of the destination
+// with 16-byte non-temporal stores of values that depend on what it read (so
+// no load can be dropped).  Of a sweep over 256-2048 workgroups of 256-1024
+// threads with 4-16 loads in flight, issued in batches or two batches
+// overlapped, this shape was within 1.6 % of the fastest at both 100 MB
+// (15.6 us) and 400 MB (59.2 us against 58.3): more workgroups than the
+// compute units hold at once let the dispatcher even out the last ones.
 #include "think_common.h"
 
 namespace thinkkv {
 namespace {
 
 constexpr int kProbeThreads = 512;
-constexpr int kProbeWgs = 512;
+constexpr int kProbeWgs = 2048;
 constexpr int kProbeUnroll = 8;
 
 __global__ __launch_bounds__(kProbeThreads) void k_probe_stream(const char* __restrict__ src,
@@ -55,9 +59,9 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_stream(const char* __re
 
 hipError_t launch_probe_stream(const void* src, size_t read_bytes, void* dst, size_t write_bytes,
                                hipStream_t s) {
-    // slices of whole 16-byte vectors
-    const size_t rd = (read_bytes / kProbeWgs + 15) / 16 * 16;
-    const size_t wr = (write_bytes / kProbeWgs + 15) / 16 * 16;
+    // slices of whole 16-byte vectors that together cover the byte counts
+    const size_t rd = ((read_bytes + kProbeWgs - 1) / kProbeWgs + 15) / 16 * 16;
+    const size_t wr = ((write_bytes + kProbeWgs - 1) / kProbeWgs + 15) / 16 * 16;
     k_probe_stream<<<kProbeWgs, kProbeThreads, 0, s>>>(static_cast<const char*>(src), rd,
                                                        read_bytes, static_cast<char*>(dst), wr,
                                                        write_bytes);
