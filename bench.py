@@ -831,7 +831,7 @@ def measure(cfg, args, torch, qdk, dev, steps, warmup, extras):
         "input_copies": wl.ncopies,
         "ceiling": {
             "probe": ("think_probe_stream: one launch that only reads (and writes) the path's "
-                      "bytes, 512 workgroups x 512 threads, back-to-back launches on rotating "
+                      "bytes, 2048 workgroups x 512 threads, back-to-back launches on rotating "
                       "windows so reads come from HBM"),
             "decode": {"read_bytes": bm["dec_call"], "us_per_launch": round(dec_ceil, 2),
                        "GBps": round(bm["dec_call"] / (dec_ceil * 1e-6) / 1e9, 1),
