@@ -388,10 +388,14 @@ int general_chunk(const think_dims& d, int keep) {
 // than 64) the floor is what gives about one workgroup per CU, between 128
 // and 512, so a small call still spreads over the chip (4K x 8 heads, keep 64:
 // 15.5 -> 12.2 us; 8K x 8 heads 16.0 -> 13.8; 4K x 32 heads keeps 512).
+// The head-dim-64 instance moves half the value bytes per 32-token step with
+// the same instructions, so its single sequences are sized for about 256
+// workgroups, one per CU (32K x 8 heads 17.7 -> 17.2 us, 128K 43.5 -> 41.9;
+// at head_dim 128, 256 workgroups lose: 128K 67.7 -> 72.2 us).
 int mfma_decode_chunk(const think_dims& d, int keep) {
     const bool balanced = d.batch >= 2 && d.batch <= 64;
     const bool three = balanced && keep % 8 == 0 && keep <= 64;
-    const int64_t wgs = three ? 768 : 512;
+    const int64_t wgs = three ? 768 : (!balanced && d.head_dim == 64 ? 256 : 512);
     const int64_t work = (int64_t)d.seq_capacity * d.n_kv_heads * d.batch;
     int64_t chunk = (work + wgs - 1) / wgs;
     const int64_t min_chunk = ((int64_t)d.seq_capacity + 255) / 256;
