@@ -9,6 +9,8 @@ head_dim, keep and the query heads per kv head): 32- and 64-token tiles,
 16-, 8- and 4-byte and one-element key units, 4 and 16 head slots, chunks of 256 tokens
 halved while the grid fits one wave of resident workgroups.  Padding rows of
 K_thin and V past each length hold NaN, so a read past len_b shows up.
+Three more shapes reach the merge kernel's column slices and a pairwise
+merge tree whose sub-group count is not a power of two.
 Bar: per row max-abs error relative to the row's max-abs, 1e-5 (fp32) and
 2e-2 (bf16), as for every decode."""
 import numpy as np
@@ -107,3 +109,18 @@ def test_full_size_decode_matches_the_oracle(shape):
     dtype, B, S, Hq, Hkv, D, keep = shape
     rng = np.random.default_rng(S + D + keep)
     _check(dtype, B, S, Hq, Hkv, D, keep, [S] * B, rng, "full-size")
+
+
+@pytest.mark.parametrize("shape", [
+    # dtype, B, S, Hq, Hkv, D, keep: chunk slot counts whose merge has a
+    # sub-group count that is not a power of two (the pairwise tree then
+    # leaves an odd sub-group over in some rounds) and records split into
+    # column slices
+    ("bf16", 1, 65536, 28, 7, 128, 64),     # matrix-core pass, 74 slots a head
+    ("f32", 1, 25600, 8, 2, 128, 48),       # general pass, about 100 slots a head
+    ("bf16", 1, 20000, 12, 3, 72, 40),      # general pass, 18 column quads in two slices
+], ids=["mfma-74-slots", "general-100-slots", "general-d72-slices"])
+def test_merge_tree_and_column_slices_match_the_oracle(shape):
+    dtype, B, S, Hq, Hkv, D, keep = shape
+    rng = np.random.default_rng(S + Hkv)
+    _check(dtype, B, S, Hq, Hkv, D, keep, [S - 37], rng, "merge-shape")
