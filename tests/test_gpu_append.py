@@ -7,7 +7,9 @@ still holds the NaN sentinel), and the attention over len_b + 1 tokens must be
 within the decode tolerance.  Cases cover ragged batches (chunk slots dealt by
 length), one long sequence, batches past the balanced range, odd keep, fp32,
 empty sequences, a sequence that fills its last slot and one already at
-capacity (left as it is, attending over its cached tokens only)."""
+capacity (left as it is, attending over its cached tokens only), and long
+sequences whose merge runs in column slices (only the first slice writes the
+new token's rows and advances the length)."""
 import numpy as np
 import pytest
 import torch
@@ -29,6 +31,8 @@ CASES = [
     (56, [0, 130], 4, 2, 32, 160, 9, "f32"),               # general decode, empty sequence
     (57, [(37 * i) % 300 for i in range(70)], 8, 2, 128, 300, 40, "bf16"),  # B past 64
     (58, [2, 1], 4, 1, 64, 2, 16, "bf16"),                 # capacity 2: both full by step 2
+    (59, [39990], 32, 8, 128, 40000, 64, "bf16"),          # merge in four column slices
+    (60, [6000], 8, 2, 256, 6100, 100, "f32"),             # general decode, sliced merge
 ]
 
 
