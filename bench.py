@@ -420,12 +420,14 @@ def probe_ceiling(torch, dev, read_bytes, write_bytes, launches=64):
     """The single-launch ceiling for a path's byte counts: back-to-back launches
     of think_probe_stream (one launch reads read_bytes and writes write_bytes
     with nothing else to do), each on a different window of a scratch buffer
-    so that the reads come from HBM.  Returns microseconds per launch."""
+    of at least 1 GiB, so that the reads come from HBM and not from the 256 MB
+    last-level cache (as the workloads' own inputs rotate over copies).
+    Returns microseconds per launch."""
     from query_driven_kv_amd import _lib
     P = ctypes.c_void_p
     r = (read_bytes + 255) // 256 * 256
     w = (write_bytes + 255) // 256 * 256
-    nwin = 4 if r < (256 << 20) else 2
+    nwin = min(4096, max(2, -(-(1 << 30) // max(r, 1))))
     src = torch.empty(max(r * nwin, 16), dtype=torch.uint8, device=dev)
     dst = torch.empty(max(w * nwin, 16), dtype=torch.uint8, device=dev)
     sp = P(torch.cuda.current_stream().cuda_stream)
