@@ -14,13 +14,18 @@ from gpu_util import to_dev
 pytestmark = pytest.mark.gpu
 
 
-def test_pruning_and_decode_step_replays_in_a_graph():
+@pytest.mark.parametrize("shape", [
+    # B, Hq, Hkv, D, S, keep, lengths
+    (2, 8, 2, 128, 3000, 64, [3000, 1777]),     # chunk slots dealt by length
+    (1, 32, 8, 128, 40000, 64, [39000]),        # merge in column slices
+], ids=["ragged-pair", "long-sliced-merge"])
+def test_pruning_and_decode_step_replays_in_a_graph(shape):
     import query_driven_kv_amd as qdk
-    B, Hq, Hkv, D, S, keep = 2, 8, 2, 128, 3000, 64
+    B, Hq, Hkv, D, S, keep, lengths = shape
     cfg = kvsynth.custom("graph", batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, seq_capacity=S,
                          obs_window=8, keep=keep, dtype="bf16", lowrank=8, cfg_id=93)
     L = kvsynth.make_layer(cfg, layer=0)
-    L["seq_lens"] = np.array([3000, 1777], np.int32)
+    L["seq_lens"] = np.array(lengths, np.int32)
     k, v, qo = to_dev(L["k_cache"]), to_dev(L["v_cache"]), to_dev(L["q_obs"])
     lens = to_dev(L["seq_lens"])
     dims = qdk.make_dims(B, Hq, Hkv, D, S, torch.bfloat16)
