@@ -335,8 +335,11 @@ __global__ __launch_bounds__(1024) void k_score_finalize(
     if (SELECT) {
         __syncthreads();
         const size_t row = (size_t)b * Hkv + kv;
-        select_row(s_sc, D, keep, s_scratch, s_cut, kept_idx + row * keep,
-                   near_tie ? near_tie + row : nullptr);
+        int32_t* const tie = near_tie ? near_tie + row : nullptr;
+        if (D == 128)
+            select_row<128>(s_sc, D, keep, nth, s_scratch, s_cut, kept_idx + row * keep, tie);
+        else
+            select_row(s_sc, D, keep, nth, s_scratch, s_cut, kept_idx + row * keep, tie);
     }
 }
 

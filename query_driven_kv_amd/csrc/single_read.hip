@@ -82,7 +82,7 @@ __device__ __forceinline__ void signal_flag(unsigned long long* f, unsigned long
 __device__ __forceinline__ void wait_flags(unsigned long long* f, int n,
                                            unsigned long long tag, unsigned long long want,
                                            uint32_t limit, unsigned long long* err) {
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    for (int i = threadIdx.x; i < n; i += kSrThreads) {
         for (uint32_t spin = 0;; ++spin) {
             if (__hip_atomic_load(f + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == want)
                 break;
@@ -118,7 +118,11 @@ struct SrParams {
     int s_cap, nvec, rpw, wps, nb, W, nqv, Hq, Hkv, D, keep;
 };
 
-template <int DT, int NV>
+// DC: head_dim fixed at compile time (128), or 0 for any head_dim; the
+// phases after the stream are chains of dependent steps, where index
+// arithmetic on a run-time head_dim (divisions, loops of unknown trip count)
+// shows up directly in the launch's duration.
+template <int DT, int NV, int DC>
 __global__ __launch_bounds__(kSrThreads) void k_score_compact_resident(SrParams p) {
     using E = Elem<DT>;
     using T = typename E::T;
@@ -257,12 +261,11 @@ __global__ __launch_bounds__(kSrThreads) void k_score_compact_resident(SrParams 
 
     // ---- phase 2: scores and selection, one workgroup per (b, kv)
     if (w < p.nb * p.Hkv) {
-        wait_flags(p.tile_done, nwg, tag, want, p.spin_limit, p.err);
-        // every workgroup has stored its flag, so every one has read gen
-        if (w == 0 && tid == 0)
-            __hip_atomic_store(p.gen, gen + 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // what does not depend on other workgroups' data (the sequence
+        // length, the index arithmetic) is done before the wait, so that the
+        // loads after it start at once
         const int bb = w / p.Hkv, kv = w - bb * p.Hkv;
-        const int D = p.D, G = p.Hq / p.Hkv, Q = D / 4, SG = kSrThreads / Q;
+        const int D = DC > 0 ? DC : p.D, G = p.Hq / p.Hkv, Q = D / 4, SG = kSrThreads / Q;
         const int lenb = clamp_len(p.seq_lens, bb, p.s_cap);
         const int np = min(p.wps, (lenb + p.rpw - 1) / p.rpw);   // tiles holding rows
         double* red2 = reinterpret_cast<double*>(lds);           // [SG][D]
@@ -271,6 +274,10 @@ __global__ __launch_bounds__(kSrThreads) void k_score_compact_resident(SrParams 
         int* scratch = reinterpret_cast<int*>(s_sc + 256);       // [512]
         float* cut = reinterpret_cast<float*>(scratch + kSrThreads);
         const int cq = tid % Q, sg = tid / Q;
+        wait_flags(p.tile_done, nwg, tag, want, p.spin_limit, p.err);
+        // every workgroup has stored its flag, so every one has read gen
+        if (w == 0 && tid == 0)
+            __hip_atomic_store(p.gen, gen + 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         // the group's window sums first, so both loads are in flight together
         const double* qs = p.q2 + ((size_t)bb * p.Hq + (size_t)kv * G) * D;
         double qv[4096 / kSrThreads];
@@ -319,8 +326,13 @@ __global__ __launch_bounds__(kSrThreads) void k_score_compact_resident(SrParams 
         __syncthreads();
         const size_t row = (size_t)bb * p.Hkv + kv;
         uint32_t* s_mask = reinterpret_cast<uint32_t*>(cut + 4);      // [8]
-        select_row(s_sc, D, p.keep, scratch, cut, p.kept_idx + row * p.keep,
-                   p.near_tie ? p.near_tie + row : nullptr, s_mask);
+        int32_t* const tie = p.near_tie ? p.near_tie + row : nullptr;
+        if (D == 128)
+            select_row<128, kSrThreads>(s_sc, D, p.keep, kSrThreads, scratch, cut,
+                                        p.kept_idx + row * p.keep, tie, s_mask);
+        else
+            select_row<0, kSrThreads>(s_sc, D, p.keep, kSrThreads, scratch, cut,
+                                      p.kept_idx + row * p.keep, tie, s_mask);
         __syncthreads();
         const int nw = (D + 15) / 16;
         if (tid < nw)
@@ -335,7 +347,21 @@ __global__ __launch_bounds__(kSrThreads) void k_score_compact_resident(SrParams 
     T* rows = reinterpret_cast<T*>(lds);                      // [SK * 512 vectors]
     uint16_t* srcmap = reinterpret_cast<uint16_t*>(lds + SK * kSrThreads);
     uint32_t* kmask = reinterpret_cast<uint32_t*>(srcmap + (Ro + 7) / 8 * 8);   // [Hkv][nw]
-    const int nw = (p.D + 15) / 16;
+    const int Dh = DC > 0 ? DC : p.D;
+    const int nw = (Dh + 15) / 16;
+    T* k_thin = static_cast<T*>(p.k_thin);
+    const int sub_rows = SK * kSrThreads / nvec;              // token rows per sub-tile
+    // Whole thin rows of 16-byte chunks (Ro*e a multiple of 16, so every row
+    // starts on a chunk): thread tid always builds chunk cp of rows rr,
+    // rr + rpp, ...; its CE source channels are the same for every row, read
+    // from the source map once.  (Worked out before the wait for the kept
+    // channels, which they do not depend on.)
+    const int cpr = Ro / CE;
+    const bool whole = Ro % CE == 0 && cpr <= kSrThreads;
+    const int rpp = whole ? kSrThreads / cpr : 1;
+    const bool builds = whole && tid < rpp * cpr;
+    const int cp = builds ? tid % cpr : 0;
+    const int rr = builds ? tid / cpr : (1 << 30);            // threads past rpp*cpr: none
     // phase 2's LDS is free once its mask chunks are published (with 4 vectors
     // per thread the arrays below start at 32 KiB and can reach them)
     __syncthreads();
@@ -362,26 +388,18 @@ __global__ __launch_bounds__(kSrThreads) void k_score_compact_resident(SrParams 
     // then hands out the next slots to its own kept channels in ascending order
     for (int i = tid; i < p.Hkv * nw; i += kSrThreads) {
         const int kv = i / nw, wi = i - kv * nw;
-        int j = 0;
-        for (int x = 0; x < wi; ++x) j += __popc(kmask[kv * nw + x]);
+        int j = 0;                               // kept channels of the chunks below
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {           // every read in range, all issued at once
+            const uint32_t w = kmask[kv * nw + (x < nw ? x : 0)];
+            j += x < wi ? __popc(w) : 0;
+        }
         for (uint32_t m = kmask[i]; m != 0u; m &= m - 1u) {
             const int c = wi * 16 + __builtin_ctz(m);
-            if (j < keep && c < p.D) srcmap[kv * keep + j] = (uint16_t)(kv * p.D + c);
+            if (j < keep && c < Dh) srcmap[kv * keep + j] = (uint16_t)(kv * Dh + c);
             ++j;
         }
     }
-    T* k_thin = static_cast<T*>(p.k_thin);
-    const int sub_rows = SK * kSrThreads / nvec;              // token rows per sub-tile
-    // Whole thin rows of 16-byte chunks (Ro*e a multiple of 16, so every row
-    // starts on a chunk): thread tid always builds chunk cp of rows rr,
-    // rr + rpp, ...; its CE source channels are the same for every row, read
-    // from the source map once.
-    const int cpr = Ro / CE;
-    const bool whole = Ro % CE == 0 && cpr <= kSrThreads;
-    const int rpp = whole ? kSrThreads / cpr : 1;
-    const bool builds = whole && tid < rpp * cpr;
-    const int cp = builds ? tid % cpr : 0;
-    const int rr = builds ? tid / cpr : (1 << 30);            // threads past rpp*cpr: none
     int src[CE];
     __syncthreads();                                          // srcmap built
 #pragma unroll
@@ -452,24 +470,25 @@ size_t sr_lds_bytes(const think_dims& d, int keep, int nv) {
 }
 
 template <int DT, int NV>
-const void* sr_kernel() {
-    return reinterpret_cast<const void*>(&k_score_compact_resident<DT, NV>);
+const void* sr_kernel(int D) {
+    return D == 128 ? reinterpret_cast<const void*>(&k_score_compact_resident<DT, NV, 128>)
+                    : reinterpret_cast<const void*>(&k_score_compact_resident<DT, NV, 0>);
 }
 
-const void* sr_kernel_for(int dtype, int nv) {
+const void* sr_kernel_for(int dtype, int nv, int D) {
     if (dtype == THINK_BF16) {
         switch (nv) {
-            case 4: return sr_kernel<THINK_BF16, 4>();
-            case 8: return sr_kernel<THINK_BF16, 8>();
-            case 16: return sr_kernel<THINK_BF16, 16>();
-            case 32: return sr_kernel<THINK_BF16, 32>();
+            case 4: return sr_kernel<THINK_BF16, 4>(D);
+            case 8: return sr_kernel<THINK_BF16, 8>(D);
+            case 16: return sr_kernel<THINK_BF16, 16>(D);
+            case 32: return sr_kernel<THINK_BF16, 32>(D);
         }
     } else {
         switch (nv) {
-            case 4: return sr_kernel<THINK_F32, 4>();
-            case 8: return sr_kernel<THINK_F32, 8>();
-            case 16: return sr_kernel<THINK_F32, 16>();
-            case 32: return sr_kernel<THINK_F32, 32>();
+            case 4: return sr_kernel<THINK_F32, 4>(D);
+            case 8: return sr_kernel<THINK_F32, 8>(D);
+            case 16: return sr_kernel<THINK_F32, 16>(D);
+            case 32: return sr_kernel<THINK_F32, 32>(D);
         }
     }
     return nullptr;
@@ -539,7 +558,7 @@ bool single_read_plan(const think_dims& d, int keep, const SingleReadGeom& g, Sr
     if (!nv) return false;
     const size_t lds = sr_lds_bytes(d, keep, nv);
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, sr_kernel_for(d.dtype, nv),
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, sr_kernel_for(d.dtype, nv, d.head_dim),
                                                      kSrThreads, lds) != hipSuccess ||
         per_cu < 1)
         return false;
@@ -588,7 +607,7 @@ hipError_t launch_single_read(const think_dims& d, const SingleReadGeom& g, cons
     p.D = d.head_dim;
     p.keep = keep;
     void* args[] = {&p};
-    return hipLaunchKernel(sr_kernel_for(d.dtype, pl.nv), dim3(d.batch * pl.wps),
+    return hipLaunchKernel(sr_kernel_for(d.dtype, pl.nv, d.head_dim), dim3(d.batch * pl.wps),
                            dim3(kSrThreads), args, pl.lds, s);
 }
 
