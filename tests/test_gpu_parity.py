@@ -214,6 +214,29 @@ def test_exact_tie_goes_to_lower_channel_and_is_flagged():
     assert a in kept and b not in kept
 
 
+def test_select_on_crafted_scores_matches_the_oracle():
+    """think_select on scores drawn from a few fp32 values (many exact ties,
+    +0 and -0, subnormals, the largest finite magnitude): kept channels and
+    near-tie flags bit-exact against the oracle's selection of the same
+    values, for head dims on both selection instances (128 and others)."""
+    qdk = _qdk()
+    rng = np.random.default_rng(77)
+    tiny = np.float32(1e-40)                                   # subnormal
+    pool = np.array([0.0, -0.0, tiny, 2 * tiny, 1.0, np.nextafter(np.float32(1), np.float32(2)),
+                     2.5, 7.0, 3.0e38], dtype=np.float32)
+    for D in (8, 64, 96, 128, 256):
+        for keep in sorted({1, max(1, D // 3), D // 2, D - 1, D}):
+            print(f"[select] D={D} keep={keep}", flush=True)
+            s = pool[rng.integers(0, len(pool), size=(2, 5, D))]
+            s[0, 0] = np.float32(2.5)                          # one value throughout
+            s[1, 1] = np.where(rng.random(D) < 0.5, np.float32(0.0), np.float32(-0.0))
+            idx, tie = qdk.think_select(to_dev(s), keep)
+            torch.cuda.synchronize()
+            o_idx, o_tie = oracle.select(s.astype(np.float64), keep)
+            np.testing.assert_array_equal(to_host(idx), o_idx)
+            np.testing.assert_array_equal(to_host(tie), o_tie)
+
+
 def test_empty_sequences_in_a_ragged_batch_decode_to_zero():
     """Matrix-core decode with chunk slots dealt by length: empty sequences
     get no slot and a zero output; the others match the oracle one by one."""
